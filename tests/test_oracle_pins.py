@@ -1,0 +1,326 @@
+"""Pins of the float64 CPU oracle to facts the H2O pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: a library
+attention routine (torch's scaled_dot_product_attention on the CPU in float64)
+for the special cases that reduce to full or sliding-window attention, closed
+forms, hand-built exact ties, exhaustive search on tiny inputs, and invariants
+of the eviction rule (summary page "H2O: Heavy-Hitter Oracle for Efficient
+Generative Inference", "The mechanism" and "Algorithm / figure walkthrough").
+"""
+import itertools
+from collections import defaultdict
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import (causal_attention, decode_step, prefill, prefill_column_sums,
+                    prefill_keep, run_trace)
+from synth import WORKLOADS, gen
+
+
+def sdpa(Q, K, V, scale, mask=None, causal=False):
+    q = torch.from_numpy(np.ascontiguousarray(Q, dtype=np.float64))[None, None]
+    k = torch.from_numpy(np.ascontiguousarray(K, dtype=np.float64))[None, None]
+    v = torch.from_numpy(np.ascontiguousarray(V, dtype=np.float64))[None, None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    return F.scaled_dot_product_attention(q, k, v, attn_mask=m, is_causal=causal,
+                                          scale=scale)[0, 0].numpy()
+
+
+def random_qkv(n, d, seed, spread=1.0):
+    rng = np.random.default_rng(seed)
+    return tuple(spread * rng.standard_normal((n, d)) for _ in range(3))
+
+
+def c1_unit(unit):
+    wl = WORKLOADS["tiny_fp32"]
+    Q, K, V = gen.unit_values(wl, 0, unit, 0, wl.n_positions)
+    return wl, Q, K, V
+
+
+TRACE_CASES = [  # (P, T, r, h, d, seed)
+    (24, 30, 4, 6, 8, 1),
+    (10, 25, 3, 5, 16, 2),
+    (5, 20, 4, 4, 8, 3),      # prompt shorter than the budget
+    (3, 15, 4, 2, 8, 4),      # prompt shorter than the protected window
+    (30, 20, 1, 7, 8, 5),     # smallest protected window
+    (16, 16, 8, 0, 8, 6),     # no heavy slots
+]
+
+
+def all_traces():
+    for (P, T, r, h, d, seed) in TRACE_CASES:
+        Q, K, V = random_qkv(P + T, d, seed, spread=1.5)
+        yield P, T, r, h, 1 / np.sqrt(d), Q, K, V
+    for unit in (0, 1):
+        wl, Q, K, V = c1_unit(unit)
+        yield wl.prompt, wl.steps, wl.recent, wl.heavy, wl.scale, Q, K, V
+
+
+# --- P1: a budget covering the whole sequence is full causal attention -------
+
+@pytest.mark.parametrize("P,T,r,h", [(12, 10, 4, 30), (5, 9, 8, 10), (3, 8, 2, 12),
+                                     (16, 4, 16, 4), (1, 6, 1, 6)])
+def test_full_budget_equals_full_causal_attention(P, T, r, h):
+    d = 8
+    N = P + T
+    assert r + h >= N
+    Q, K, V = random_qkv(N, d, seed=P * 100 + T, spread=2.0)
+    scale = 1 / np.sqrt(d)
+    seeded, c, steps = run_trace(Q, K, V, P, T, r, h, scale)
+
+    A_prompt = sdpa(Q[:P], K[:P], np.eye(P), scale, causal=True)
+    assert sorted(seeded) == list(range(P))
+    np.testing.assert_allclose([seeded[j] for j in range(P)], A_prompt.sum(0),
+                               rtol=1e-12, atol=1e-13)
+
+    ref_out = sdpa(Q, K, V, scale, causal=True)
+    for s, res in enumerate(steps):
+        t = P + s
+        assert res.evicted is None
+        np.testing.assert_allclose(res.out, ref_out[t], rtol=1e-12, atol=1e-12)
+
+    A = sdpa(Q, K, np.eye(N), scale, causal=True)   # full attention matrix
+    final = steps[-1].members
+    assert sorted(final) == list(range(N))
+    np.testing.assert_allclose([final[j] for j in range(N)], A.sum(0),
+                               rtol=1e-12, atol=1e-13)
+
+
+# --- P2: no heavy slots is sliding-window (Local) attention ------------------
+
+@pytest.mark.parametrize("P,T,k", [(16, 20, 6), (3, 12, 6), (6, 6, 6), (10, 10, 1)])
+def test_zero_heavy_equals_sliding_window(P, T, k):
+    d = 8
+    N = P + T
+    Q, K, V = random_qkv(N, d, seed=7 + k, spread=2.0)
+    scale = 1 / np.sqrt(d)
+    _, _, steps = run_trace(Q, K, V, P, T, k, 0, scale)
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    band = (j <= i) & (j >= i - k)
+    ref = sdpa(Q, K, V, scale, mask=band)
+    for s, res in enumerate(steps):
+        t = P + s
+        assert res.evicted == (t - k if t >= k else None)
+        np.testing.assert_allclose(res.out, ref[t], rtol=1e-12, atol=1e-12)
+
+
+# --- P3: Definition 4.3 and irreversible eviction ----------------------------
+
+def test_definition_4_3_invariants():
+    for P, T, r, h, scale, Q, K, V in all_traces():
+        k = r + h
+        seeded, _, steps = run_trace(Q, K, V, P, T, r, h, scale)
+        prev = set(seeded)
+        assert len(prev) == min(P, k)
+        gone = set()
+        for s, res in enumerate(steps):
+            t = P + s
+            cur = set(res.members)
+            assert len(cur) == min(t + 1, k)
+            assert cur <= prev | {t}
+            assert len(cur - prev) <= 1
+            assert set(range(max(0, t - r + 1), t + 1)) <= cur
+            assert not (cur & gone)
+            if res.evicted is not None:
+                assert res.evicted in prev and res.evicted not in cur
+                gone.add(res.evicted)
+            assert (prev | {t}) - cur == ({res.evicted} if res.evicted is not None else set())
+            prev = cur
+
+
+# --- P4: score bounds; P9: mass conservation ---------------------------------
+
+def test_score_bounds_and_mass_conservation():
+    for P, T, r, h, scale, Q, K, V in all_traces():
+        seeded, _, steps = run_trace(Q, K, V, P, T, r, h, scale)
+        evicted_any = len(seeded) < P
+        prev = seeded
+        total_prev = sum(seeded.values())
+        if not evicted_any:
+            assert total_prev == pytest.approx(P, rel=1e-12)
+        for s, res in enumerate(steps):
+            t = P + s
+            vals = np.array(list(res.members.values()))
+            assert (vals >= 0).all()
+            total = vals.sum()
+            assert total <= (t + 1) * (1 + 1e-12)
+            if res.evicted is None:
+                assert total == pytest.approx(total_prev + 1, rel=1e-12)
+            else:
+                evicted_any = True
+                victim_score = prev[res.evicted] + res.weights[res.evicted]
+                assert total == pytest.approx(total_prev + 1 - victim_score, rel=1e-12)
+            if not evicted_any:
+                assert total == pytest.approx(t + 1, rel=1e-12)
+            total_prev = total
+            prev = res.members
+
+
+# --- P5: brute-force recomputation of the accumulated scores -----------------
+
+def test_scores_match_non_incremental_recomputation():
+    for P, T, r, h, scale, Q, K, V in all_traces():
+        seeded, _, steps = run_trace(Q, K, V, P, T, r, h, scale)
+        A_prompt = sdpa(Q[:P], K[:P], np.eye(P), scale, causal=True)
+        acc = defaultdict(float)
+        for j, cj in enumerate(A_prompt.sum(0)):
+            acc[j] = cj
+        for s, res in enumerate(steps):
+            t = P + s
+            idx = res.attended
+            w = torch.softmax(torch.from_numpy(scale * (K[idx] @ Q[t])), dim=0).numpy()
+            for j, wj in zip(idx, w):
+                acc[j] += wj
+            for j, sc in res.members.items():
+                assert sc == pytest.approx(acc[j], rel=1e-11, abs=1e-13)
+
+
+# --- P6: the eviction maximises the retained accumulated score ---------------
+
+def test_eviction_is_greedy_max_retained_mass():
+    for P, T, r, h, scale, Q, K, V in all_traces():
+        seeded, _, steps = run_trace(Q, K, V, P, T, r, h, scale)
+        prev = seeded
+        for s, res in enumerate(steps):
+            t = P + s
+            pre = {j: prev[j] + res.weights[j] for j in prev}
+            pre[t] = res.weights[t]
+            if res.evicted is not None:
+                cands = [j for j in pre if j <= t - r]
+                kept_mass = {v: sum(sc for j, sc in pre.items() if j != v) for v in cands}
+                best = max(kept_mass.values())
+                # greatest retained mass; among equal masses the older goes
+                winners = sorted(v for v in cands if kept_mass[v] == best)
+                assert res.evicted == winners[0]
+            prev = res.members
+
+
+# --- P7: closed form under uniform attention ----------------------------------
+
+def test_uniform_attention_closed_form():
+    P, T, r, h, d = 64, 64, 16, 16, 8
+    k = r + h
+    N = P + T
+    rng = np.random.default_rng(11)
+    Q = np.zeros((N, d))
+    K = rng.standard_normal((N, d))
+    V = rng.standard_normal((N, d))
+    seeded, c, steps = run_trace(Q, K, V, P, T, r, h, 1 / np.sqrt(d))
+    H = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, N + 1))])   # harmonic numbers
+    np.testing.assert_allclose(c, H[P] - H[np.arange(P)], rtol=1e-13)
+    assert sorted(seeded) == list(range(h)) + list(range(P - r, P))
+    for s, res in enumerate(steps):
+        t = P + s
+        assert res.evicted == t - r
+        att = list(range(h)) + list(range(t - r, t + 1))
+        np.testing.assert_allclose(res.out, V[att].mean(0), rtol=1e-12, atol=1e-13)
+    final = steps[-1].members
+    assert sorted(final) == list(range(h)) + list(range(N - r, N))
+    for j, sc in final.items():
+        expect = (H[P] - H[j] if j < P else 0.0) + (N - max(j, P)) / (k + 1)
+        assert sc == pytest.approx(expect, rel=1e-12)
+
+
+# --- P8: exact ties -------------------------------------------------------------
+
+def test_prefill_and_decode_exact_ties_from_dead_keys():
+    """Keys far below the row maximum get weight exactly 0.0 in float64, so
+    several positions tie at score 0: prefill keeps the newer ones, decode
+    evicts the older ones first."""
+    d, P, r, h = 8, 24, 4, 6
+    alive_pool = {0, 4, 9, 15}
+    N = P + 4
+    e0 = np.eye(d)[0]
+    Q = np.tile(e0, (N, 1))
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((N, d))
+    K[:, 0] = 0.0                       # alive keys: logit exactly 0
+    dead = [j for j in range(P - r) if j not in alive_pool]
+    K[dead] = -1e4 * e0                 # dead keys: weight underflows to exactly 0
+    V = rng.standard_normal((N, d))
+    scale = 1 / np.sqrt(d)
+    seeded, c, steps = run_trace(Q, K, V, P, N - P, r, h, scale)
+    assert all(c[j] == 0.0 for j in dead)
+    assert all(c[j] > 0.0 for j in alive_pool)
+    assert sorted(seeded) == sorted(alive_pool) + [18, 19] + list(range(P - r, P))
+    assert steps[0].evicted == 18
+    assert steps[1].evicted == 19
+    assert all(res.evicted not in alive_pool for res in steps)
+
+
+def test_decode_exact_tie_evicts_oldest():
+    r, h = 2, 5
+    members = {0: 0.5, 1: 0.25, 2: 0.25, 3: 0.25, 4: 0.75, 5: 0.25, 6: 0.125}
+    d = 4
+    t = 7
+    rng = np.random.default_rng(3)
+    K = rng.standard_normal((t + 1, d))
+    V = rng.standard_normal((t + 1, d))
+    res = decode_step(members, t, np.zeros(d), K, V, r, h, 0.5)
+    assert res.evicted == 1
+    scores = [res.members[j] for j in (2, 3, 5)]
+    assert scores[0] == scores[1] == scores[2] == 0.25 + 1 / 8
+
+
+def test_prefill_keep_exhaustive_on_tiny_inputs():
+    rng = np.random.default_rng(9)
+    for trial in range(200):
+        P = int(rng.integers(1, 11))
+        r = int(rng.integers(1, 4))
+        h = int(rng.integers(0, 5))
+        c = rng.integers(0, 4, size=P).astype(float)     # small integers: many exact ties
+        keep = prefill_keep(c, r, h)
+        if P <= r + h:
+            assert keep == list(range(P))
+            continue
+        pool = list(range(P - r))
+        best = max(itertools.combinations(pool, h),
+                   key=lambda S: (sum(c[j] for j in S), sum(S)))
+        assert keep == sorted(best) + list(range(P - r, P))
+
+
+# --- P10: accumulation matters (naive per-step top-k is a different rule) ------
+
+def test_not_naive_per_step_top_k():
+    wl, Q, K, V = c1_unit(0)
+    seeded, _, steps = run_trace(Q, K, V, wl.prompt, wl.steps, wl.recent, wl.heavy, wl.scale)
+    prev = seeded
+    differ = 0
+    for s, res in enumerate(steps):
+        t = wl.prompt + s
+        cands = [j for j in list(prev) + [t] if j <= t - wl.recent]
+        naive = min(cands, key=lambda j: (res.weights[j], j))
+        differ += naive != res.evicted
+        prev = res.members
+    assert differ >= 1
+
+
+# --- prefill column sums: consistency with the attention matrix ----------------
+
+def test_prefill_column_sums_sum_to_prompt_length():
+    for n in (1, 2, 7, 64):
+        Q, K, _ = random_qkv(n, 16, seed=n, spread=3.0)
+        c = prefill_column_sums(Q, K, 0.25)
+        assert c.sum() == pytest.approx(n, rel=1e-13)
+        A = causal_attention(Q, K, 0.25)
+        np.testing.assert_allclose(A, sdpa(Q, K, np.eye(n), 0.25, causal=True), atol=1e-14)
+        assert c[-1] == pytest.approx(A[-1, -1])
+
+
+# --- regression record of the tiny fp32 trajectory -------------------------------
+
+def test_tiny_trace_matches_recorded_trajectory():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_fp32_trace.json")
+    rec = json.load(open(path))
+    for u in rec["units"]:
+        wl, Q, K, V = c1_unit(u["head"])
+        seeded, _, steps = run_trace(Q, K, V, wl.prompt, wl.steps, wl.recent, wl.heavy, wl.scale)
+        assert sorted(seeded) == u["prefill_kept"]
+        assert [s.evicted for s in steps] == u["evicted"]
+        assert sorted(steps[-1].members) == u["final_members"]
