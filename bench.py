@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Decode-step throughput of the H2O hot path on one MI355X.
+
+A step is one h2o_decode_step over the whole batch of a workload: attention over
+the k cached slots plus the new token for every (batch, head) unit, score
+accumulation, eviction and admission.  Inputs are seeded synthetic tensors
+already resident in HBM before the timed region; the prefill that seeds the
+cache runs (and is timed) separately.
+
+Prints one JSON line.  `value` is decode steps/s; `roofline` reports the decode
+kernel's algorithmic bytes per launch divided by its mean launch duration
+(HIP events around every launch on the stream it runs on) against the 8 TB/s
+HBM peak; `cpu_baseline` is the float64 oracle timed on the host's cores on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload opt30b] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from synth import WORKLOADS, HEADLINE  # noqa: E402
+
+METRIC = "H2O decode steps/s + achieved HBM GB/s (% peak), OPT-30B-shape heads, 20% KV"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_MFMA_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SOURCES = ["kv_cache_eviction_02_amd/csrc/decode.hip", "kv_cache_eviction_02_amd/csrc/common.h"]
+
+
+def alg_bytes_per_step(wl):
+    """Bytes one decode step must move at minimum: every live K and V row, the
+    score read and write, q/k/v of the new token, the fp32 output, one admitted
+    row (K, V, score, position) and the evicted position."""
+    U, k, d, e = wl.units, wl.k, wl.head_dim, wl.elem_bytes
+    return (U * k * d * e * 2 + U * k * 8 + U * 3 * d * e + U * d * 4
+            + U * (2 * d * e + 8) + U * 4)
+
+
+def prefill_flops(wl):
+    """Causal QK^T of the prompt: P(P+1)/2 dot products of length d per unit."""
+    P = wl.prompt
+    return wl.units * P * (P + 1) * wl.head_dim
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_for(wl_name, waves):
+    """Measured HBM bytes per decode launch, if recorded for the current source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(wl_name)
+    if not ent or ent.get("source_sha256") != decode_source_hash() or ent.get("decode_waves") != waves:
+        return None
+    return ent.get("traffic_bytes_per_launch")
+
+
+# ---- CPU baseline: the oracle on the host cores (runs before any GPU use) -------
+
+def _oracle_worker(args):
+    wl_name, units, steps = args
+    from threadpoolctl import threadpool_limits
+    from oracle import decode_step, prefill
+    from synth import WORKLOADS as W, gen
+    wl = W[wl_name]
+    with threadpool_limits(1):
+        data = []
+        for u in units:
+            b, h = divmod(u, wl.heads)
+            Q, K, V = gen.unit_values(wl, b, h, 0, wl.prompt + steps)
+            m, _ = prefill(Q[:wl.prompt], K[:wl.prompt], wl.recent, wl.heavy, wl.scale)
+            data.append((Q, K, V, m))
+        t0 = time.perf_counter()
+        for Q, K, V, m in data:
+            for s in range(steps):
+                t = wl.prompt + s
+                m = decode_step(m, t, Q[t], K, V, wl.recent, wl.heavy, wl.scale).members
+        dt = time.perf_counter() - t0
+    return len(units) * steps, dt
+
+
+def cpu_baseline(wl, units_per_worker, steps):
+    import multiprocessing as mp
+    workers = min(16, len(os.sched_getaffinity(0)))
+    stride = max(1, wl.units // (workers * units_per_worker))
+    chosen = list(range(0, wl.units, stride))[:workers * units_per_worker]
+    jobs = [(wl.name, chosen[i::workers], steps) for i in range(workers)]
+    jobs = [j for j in jobs if j[1]]
+    with mp.get_context("fork").Pool(len(jobs)) as pool:
+        res = pool.map(_oracle_worker, jobs)
+    unit_steps_per_s = sum(n / dt for n, dt in res)
+    cpu_work = sum(dt for _, dt in res)
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": unit_steps_per_s / wl.units,
+        "unit": "steps/s",
+        "cores": len(jobs),
+        "kind": "oracle",
+        "sample": (f"{len(chosen)} of {wl.units} (batch, head) units x {steps} decode steps "
+                   f"after an untimed oracle prefill, float64 numpy, {len(jobs)} processes with one "
+                   f"BLAS thread each; {cpu_work:.1f} s of CPU time; rate scaled to whole-batch "
+                   f"steps/s; host CPU: {model}"),
+    }
+
+
+# ---- GPU -----------------------------------------------------------------------
+
+def run_gpu(wl, steps, warmup, waves):
+    import torch
+    from kv_cache_eviction_02_amd import H2OCache
+    from kv_cache_eviction_02_amd.binding import load_library
+    from synth.stage import stage_decode, stage_prompt
+
+    load_library()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    dtype = torch.bfloat16 if wl.kv_dtype == "bf16" else torch.float32
+    t0 = time.time()
+    prompt = stage_prompt(wl, dev)
+    dq, dk, dv = stage_decode(wl, 0, warmup + steps, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] staged inputs in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    cache = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy, wl.prompt, dtype,
+                     wl.scale, device=dev, decode_waves=waves)
+    stream = torch.cuda.current_stream()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    cache.prefill(*prompt)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    prefill_ms = p0.elapsed_time(p1)
+    del prompt
+
+    for s in range(warmup):
+        cache.step(dq[s], dk[s], dv[s])
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    r0.record(stream)
+    for i in range(steps):
+        s = warmup + i
+        starts[i].record(stream)
+        cache.step(dq[s], dk[s], dv[s])
+        ends[i].record(stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    region_ms = r0.elapsed_time(r1)
+    launch_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    waves_used = waves
+    if waves == 0:
+        waves_used = decode_waves_auto(wl.units)
+    cache.close()
+    return dict(region_ms=region_ms, launch_ms=launch_ms, prefill_ms=prefill_ms,
+                waves=waves_used, device=torch.cuda.get_device_name(0))
+
+
+def decode_waves_auto(units):
+    # mirrors the library's automatic choice, for reporting only
+    w = 1
+    while w < 8 and units * w * 2 <= 4096:
+        w *= 2
+    return w
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=24)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--decode-waves", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-units-per-worker", type=int, default=16)
+    ap.add_argument("--cpu-steps", type=int, default=64)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the H2O decode path has no cross-GPU exchange "
+              "((batch, head) units are independent), so only --gpus 1 is supported.",
+              file=sys.stderr)
+        sys.exit(2)
+    wl = WORKLOADS[args.workload]
+    steps = args.steps
+    warmup = args.warmup
+    if warmup + steps > wl.steps:
+        steps = max(1, wl.steps - warmup)
+        print(f"[bench] {wl.name} has {wl.steps} decode positions: timing {steps} steps",
+              file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(wl, args.cpu_units_per_worker, min(args.cpu_steps, wl.steps))
+        print(f"[bench] cpu baseline done in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    g = run_gpu(wl, steps, warmup, args.decode_waves)
+    ms_per_step = g["region_ms"] / steps
+    mean_launch_ms = sum(g["launch_ms"]) / len(g["launch_ms"])
+    bytes_step = alg_bytes_per_step(wl)
+    achieved = bytes_step / (mean_launch_ms * 1e-3) / 1e9
+    traffic = traffic_for(wl.name, g["waves"])
+    line = {
+        "metric": METRIC,
+        "value": 1e3 / ms_per_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "head_dim": wl.head_dim,
+            "prompt": wl.prompt, "k": wl.k, "recent": wl.recent, "heavy": wl.heavy,
+            "kv_dtype": wl.kv_dtype, "decode_waves": g["waves"], "parallelism": "none",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "kernel": "decode_kernel",
+            "alg_bytes_per_launch": bytes_step,
+            "mean_launch_us": mean_launch_ms * 1e3,
+        },
+        "prefill": {
+            "ms": g["prefill_ms"],
+            "qk_tflops": prefill_flops(wl) / (g["prefill_ms"] * 1e-3) / 1e12,
+            "peak_tflops": PEAK_BF16_TFLOPS if wl.kv_dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS,
+        },
+        "cpu_baseline": cpu,
+        "device": g["device"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

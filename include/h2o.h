@@ -1,0 +1,137 @@
+/*
+ * h2o.h - C ABI of the H2O (Heavy-Hitter Oracle) KV-cache hot path on MI355X (gfx950).
+ *
+ * What the calls compute follows the H2O pages: the summary "H2O: Heavy-Hitter
+ * Oracle for Efficient Generative Inference" (sections "The mechanism" with its
+ * Definition 4.3, and "Algorithm / figure walkthrough", steps 1-5) and the
+ * paper's abstract.  Per (batch, head) unit the cache holds at most
+ * k = recent + heavy key/value rows:
+ *
+ *   - the token being decoded attends over the cached rows and itself;
+ *   - every softmax weight is added into that row's accumulated score, and the
+ *     new token starts with its own weight;
+ *   - the new token is admitted; when that makes k + 1 members, the member with
+ *     the lowest score among those outside the protected window of the
+ *     `recent` newest positions (the current one included) is evicted, the
+ *     older position first on equal scores; so at most one membership change
+ *     happens per step (Definition 4.3).
+ *
+ * The prefill seeds the scores with the column sums of the prompt's exact causal
+ * attention and keeps the newest `recent` prompt positions plus the `heavy`
+ * best-scoring older ones (ties keep the newer position); a prompt no longer
+ * than k is kept whole.
+ *
+ * Slot layout (caller-owned state, row-major, contiguous):
+ *   k_slots, v_slots : [batch, heads, k, head_dim] in kv_dtype
+ *   score            : [batch, heads, k] float32, accumulated attention
+ *   pos              : [batch, heads, k] int32, absolute position, -1 = empty
+ *   slots [0, recent)  form a ring: position p lives in slot p % recent;
+ *   slots [recent, k)  hold heavy hitters, filled from slot `recent` upward.
+ *   An eviction overwrites at most two rows in place; nothing is moved.
+ *
+ * Conventions
+ *   - Pointers to tensors are HIP device pointers, 16-byte aligned (evicted_pos:
+ *     4-byte aligned), else H2O_ERR_INVALID; config/state structs and the ctx
+ *     are host memory.  `stream` is a hipStream_t (NULL = default
+ *     stream).  Every call that touches device memory only enqueues work on
+ *     `stream` and returns without synchronising.
+ *   - All arguments are validated before any HIP call; on an error return the
+ *     state buffers and the ctx counters are unchanged.
+ *   - A ctx is not thread-safe; calls on one ctx must be serialised by the
+ *     caller, and consecutive calls must go to the same stream (or be ordered
+ *     by the caller) because each step reads what the previous one wrote.
+ *   - Device faults are reported by the caller's next synchronisation.
+ */
+#ifndef H2O_H
+#define H2O_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct h2o_ctx h2o_ctx; /* opaque, library-owned */
+
+typedef enum {
+  H2O_OK = 0,
+  H2O_ERR_INVALID = 1,     /* null pointer, size or range out of bounds */
+  H2O_ERR_UNSUPPORTED = 2, /* head_dim not in {64, 96, 128}, k above the kernel limit */
+  H2O_ERR_STATE = 3,       /* call order: decode before any prefill/adopted state, position overflow */
+  H2O_ERR_OOM = 4,         /* scratch allocation failed */
+  H2O_ERR_HIP = 5          /* a HIP runtime call or launch failed */
+} h2o_status;
+
+typedef enum { H2O_F32 = 0, H2O_BF16 = 1 } h2o_dtype;
+
+/* Largest budget k = recent + heavy the decode kernel accepts (its per-row
+ * logits live in LDS). */
+#define H2O_MAX_K 8192
+
+typedef struct {
+  int32_t batch;       /* >= 1 */
+  int32_t heads;       /* >= 1 */
+  int32_t head_dim;    /* 64, 96 or 128 */
+  int32_t recent;      /* r >= 1: size of the protected window (includes the decoded token) */
+  int32_t heavy;       /* h >= 0: heavy-hitter slots; k = r + h <= H2O_MAX_K */
+  int32_t max_prompt;  /* >= 0: longest prompt h2o_prefill will accept (sizes the scratch) */
+  int32_t kv_dtype;    /* h2o_dtype of q, k, v inputs and of the K/V slots */
+  float scale;         /* softmax scale; 0 selects 1/sqrt(head_dim) */
+  int32_t start_pos;   /* adopt an existing state: position of the next token to decode */
+  int32_t start_live;  /* adopt an existing state: number of live slots (0 = no state yet) */
+  int32_t decode_waves;/* wavefronts per (batch, head) unit in the decode kernel: 0 = automatic, else 1, 2, 4 or 8 */
+} h2o_config;
+
+typedef struct {
+  void* k_slots;       /* [B, H, k, d] kv_dtype, device */
+  void* v_slots;       /* [B, H, k, d] kv_dtype, device */
+  float* score;        /* [B, H, k] float32, device */
+  int32_t* pos;        /* [B, H, k] int32, device */
+} h2o_state;
+
+/* Create a context bound to a caller-owned state.  Allocates the prefill
+ * scratch (column sums and row statistics, 3 * B * H * max_prompt floats) with
+ * hipMalloc on the current device; the state buffers are neither allocated nor
+ * touched.  With start_live > 0 the ctx adopts the state already in the
+ * buffers: it must satisfy min(start_pos, recent) <= start_live <= min(start_pos, k),
+ * start_live == start_pos when start_pos < recent, and the slot layout above.
+ * On success *out receives the ctx; on error *out is left unchanged. */
+h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** out);
+
+/* Prefill from a prompt of prompt_len tokens (summary, "Algorithm / figure
+ * walkthrough", step 1).  q, k, v: [B, H, prompt_len, d] kv_dtype, device,
+ * read only.  Overwrites the whole state: scores become the causal-attention
+ * column sums of the kept positions, K/V rows are copied into their slots,
+ * unused slots get pos = -1 and score = 0.  Afterwards the next decoded
+ * position is prompt_len.  1 <= prompt_len <= max_prompt, else
+ * H2O_ERR_INVALID.  Three kernels on `stream`. */
+h2o_status h2o_prefill(h2o_ctx* ctx, const void* q, const void* k, const void* v,
+                       int32_t prompt_len, void* stream);
+
+/* One decode step for every unit (summary, "Algorithm / figure walkthrough",
+ * steps 2-4; "The mechanism", H2O eviction).  q, k_new, v_new: [B, H, d]
+ * kv_dtype, device, the token at the current position t.  out: [B, H, d]
+ * float32, device, receives the attention output.  evicted_pos: [B, H] int32,
+ * device, receives the evicted absolute position or -1; may be NULL.  Updates
+ * score/pos/K/V in place and advances t by one.  One kernel on `stream`;
+ * allocates nothing.  H2O_ERR_STATE before any prefill or adopted state, or
+ * when t would exceed INT32_MAX - 1. */
+h2o_status h2o_decode_step(h2o_ctx* ctx, const void* q, const void* k_new, const void* v_new,
+                           float* out, int32_t* evicted_pos, void* stream);
+
+/* Host-side counters: position of the next token to decode and number of live
+ * slots per unit (the same for every unit).  Either pointer may be NULL. */
+h2o_status h2o_query(const h2o_ctx* ctx, int32_t* next_pos, int32_t* n_live);
+
+/* Free the scratch and the ctx.  NULL-safe.  Never frees caller buffers.  The
+ * caller must make sure no enqueued work still uses the ctx's scratch. */
+h2o_status h2o_destroy(h2o_ctx* ctx);
+
+/* Static description of a status code. */
+const char* h2o_status_string(h2o_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H2O_H */

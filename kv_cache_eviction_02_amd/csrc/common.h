@@ -1,0 +1,76 @@
+// Internal helpers shared by the H2O kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h2o {
+
+// Storage tag for bfloat16 elements (raw 16-bit patterns).
+struct bf16 {
+  uint16_t bits;
+};
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  static constexpr int kPer16B = 4;  // elements per 16-byte chunk
+  static constexpr int kBytes = 4;
+  // 16 raw bytes -> 4 floats
+  __device__ static inline void unpack(const uint4& raw, float* x) {
+    x[0] = __uint_as_float(raw.x);
+    x[1] = __uint_as_float(raw.y);
+    x[2] = __uint_as_float(raw.z);
+    x[3] = __uint_as_float(raw.w);
+  }
+};
+
+template <>
+struct Elem<bf16> {
+  static constexpr int kPer16B = 8;
+  static constexpr int kBytes = 2;
+  // 16 raw bytes -> 8 floats; element 2i is the low half of word i.
+  __device__ static inline void unpack(const uint4& raw, float* x) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+__device__ inline uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ inline void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// DPP lane permutations (row = 16 lanes).
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140; // lane i <- lane 15-i within a row
+constexpr int kDppHalfMirror = 0x141;// lane i <- lane 7-i within each half row
+
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G consecutive lanes; every lane of a group gets the total.
+template <int G>
+__device__ inline float group_sum(float x) {
+  static_assert(G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "group size");
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  if constexpr (G >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (G >= 16) x += dpp<kDppRowMirror>(x);
+  if constexpr (G >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (G >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace h2o

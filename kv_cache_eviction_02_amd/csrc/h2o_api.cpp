@@ -1,0 +1,196 @@
+// C ABI of the H2O hot path: argument validation, host-side position counters,
+// prefill scratch ownership, and kernel launches.  Declarations and the full
+// contract are in include/h2o.h.
+#include "h2o.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <new>
+
+#include "launch.h"
+
+struct h2o_ctx {
+  h2o_config cfg;
+  h2o_state st;
+  int32_t k;
+  int32_t waves;
+  float scale_log2;
+  int32_t t;        // absolute position of the next token to decode
+  int32_t n_live;   // live slots per unit
+  bool has_state;
+  int32_t stride;   // scratch row stride (floats)
+  float* scratch;   // 3 * units * stride floats: row max, row inverse sum, column sums
+};
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool valid_dims(const h2o_config* c) {
+  return c->batch >= 1 && c->heads >= 1 && c->recent >= 1 && c->heavy >= 0 &&
+         c->max_prompt >= 0 && (c->kv_dtype == H2O_F32 || c->kv_dtype == H2O_BF16) &&
+         isfinite(c->scale) && c->scale >= 0.f && c->start_pos >= 0 && c->start_live >= 0 &&
+         (c->decode_waves == 0 || c->decode_waves == 1 || c->decode_waves == 2 ||
+          c->decode_waves == 4 || c->decode_waves == 8);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+h2o_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return H2O_OK;
+  if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return H2O_ERR_OOM;
+  return H2O_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** out) {
+  if (!cfg || !state || !out) return H2O_ERR_INVALID;
+  if (!state->k_slots || !state->v_slots || !state->score || !state->pos) return H2O_ERR_INVALID;
+  if (!aligned16(state->k_slots) || !aligned16(state->v_slots) || !aligned16(state->score) ||
+      !aligned16(state->pos))
+    return H2O_ERR_INVALID;
+  if (!valid_dims(cfg)) return H2O_ERR_INVALID;
+  if (cfg->head_dim != 64 && cfg->head_dim != 96 && cfg->head_dim != 128) return H2O_ERR_UNSUPPORTED;
+  const int64_t k = (int64_t)cfg->recent + cfg->heavy;
+  if (k > H2O_MAX_K) return H2O_ERR_UNSUPPORTED;
+  const int64_t units = (int64_t)cfg->batch * cfg->heads;
+  if (units > INT32_MAX / 8) return H2O_ERR_INVALID;   // grid size and 32-bit index headroom
+  // Adopted state: the ring must hold min(t, r) rows and at most k are live.
+  const int32_t t0 = cfg->start_pos, n0 = cfg->start_live;
+  if (n0 == 0) {
+    if (t0 != 0) return H2O_ERR_INVALID;
+  } else {
+    const int64_t ring = t0 < cfg->recent ? t0 : cfg->recent;
+    const int64_t cap = t0 < k ? t0 : k;
+    if (n0 < ring || n0 > cap) return H2O_ERR_INVALID;
+    if (t0 >= INT32_MAX - 1) return H2O_ERR_STATE;
+  }
+
+  h2o_ctx* c = new (std::nothrow) h2o_ctx();
+  if (!c) return H2O_ERR_OOM;
+  c->cfg = *cfg;
+  c->st = *state;
+  c->k = (int32_t)k;
+  c->waves = cfg->decode_waves ? cfg->decode_waves : h2o::decode_waves_auto((int)units);
+  const float scale = cfg->scale > 0.f ? cfg->scale : 1.f / sqrtf((float)cfg->head_dim);
+  c->scale_log2 = scale * kLog2e;
+  c->t = t0;
+  c->n_live = n0;
+  c->has_state = n0 > 0;
+  c->stride = (cfg->max_prompt + 15) / 16 * 16;
+  c->scratch = nullptr;
+  if (cfg->max_prompt > 0) {
+    const size_t bytes = (size_t)3 * units * c->stride * sizeof(float);
+    const hipError_t e = hipMalloc((void**)&c->scratch, bytes);
+    if (e != hipSuccess) {
+      delete c;
+      return from_hip(e);
+    }
+  }
+  *out = c;
+  return H2O_OK;
+}
+
+h2o_status h2o_prefill(h2o_ctx* ctx, const void* q, const void* k, const void* v,
+                       int32_t prompt_len, void* stream) {
+  if (!ctx || !q || !k || !v) return H2O_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return H2O_ERR_INVALID;
+  if (prompt_len < 1 || prompt_len > ctx->cfg.max_prompt) return H2O_ERR_INVALID;
+  const size_t units = (size_t)ctx->cfg.batch * ctx->cfg.heads;
+  if ((int64_t)((prompt_len + 63) / 64) * (int64_t)units > INT32_MAX) return H2O_ERR_INVALID;
+  h2o::PrefillArgs a;
+  a.pq = q;
+  a.pk = k;
+  a.pv = v;
+  a.k_slots = ctx->st.k_slots;
+  a.v_slots = ctx->st.v_slots;
+  a.score = ctx->st.score;
+  a.pos = ctx->st.pos;
+  a.row_max = ctx->scratch;
+  a.row_inv = ctx->scratch + units * ctx->stride;
+  a.colsum = ctx->scratch + 2 * units * ctx->stride;
+  a.units = (int32_t)units;
+  a.stride = ctx->stride;
+  a.P = prompt_len;
+  a.k = ctx->k;
+  a.r = ctx->cfg.recent;
+  a.h = ctx->cfg.heavy;
+  a.scale_log2 = ctx->scale_log2;
+  const hipError_t e = h2o::launch_prefill(a, ctx->cfg.kv_dtype, ctx->cfg.head_dim,
+                                           (hipStream_t)stream);
+  if (e != hipSuccess) return from_hip(e);
+  ctx->t = prompt_len;
+  ctx->n_live = prompt_len < ctx->k ? prompt_len : ctx->k;
+  ctx->has_state = true;
+  return H2O_OK;
+}
+
+h2o_status h2o_decode_step(h2o_ctx* ctx, const void* q, const void* k_new, const void* v_new,
+                           float* out, int32_t* evicted_pos, void* stream) {
+  if (!ctx || !q || !k_new || !v_new || !out) return H2O_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) ||
+      ((uintptr_t)evicted_pos & 3u) != 0)
+    return H2O_ERR_INVALID;
+  if (!ctx->has_state) return H2O_ERR_STATE;
+  if (ctx->t >= INT32_MAX - 1) return H2O_ERR_STATE;
+  const int32_t r = ctx->cfg.recent;
+  const int32_t n_ring = ctx->t < r ? ctx->t : r;
+  h2o::DecodeArgs a;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_slots = ctx->st.k_slots;
+  a.v_slots = ctx->st.v_slots;
+  a.score = ctx->st.score;
+  a.pos = ctx->st.pos;
+  a.out = out;
+  a.evicted = evicted_pos;
+  a.units = ctx->cfg.batch * ctx->cfg.heads;
+  a.k = ctx->k;
+  a.r = r;
+  a.t = ctx->t;
+  a.n_ring = n_ring;
+  a.n_heavy = ctx->n_live - n_ring;
+  a.scale_log2 = ctx->scale_log2;
+  const hipError_t e = h2o::launch_decode(a, ctx->cfg.kv_dtype, ctx->cfg.head_dim, ctx->waves,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return from_hip(e);
+  ctx->t += 1;
+  if (ctx->n_live < ctx->k) ctx->n_live += 1;
+  return H2O_OK;
+}
+
+h2o_status h2o_query(const h2o_ctx* ctx, int32_t* next_pos, int32_t* n_live) {
+  if (!ctx) return H2O_ERR_INVALID;
+  if (next_pos) *next_pos = ctx->t;
+  if (n_live) *n_live = ctx->n_live;
+  return H2O_OK;
+}
+
+h2o_status h2o_destroy(h2o_ctx* ctx) {
+  if (!ctx) return H2O_OK;
+  hipError_t e = hipSuccess;
+  if (ctx->scratch) e = hipFree(ctx->scratch);
+  delete ctx;
+  return from_hip(e);
+}
+
+const char* h2o_status_string(h2o_status status) {
+  switch (status) {
+    case H2O_OK: return "ok";
+    case H2O_ERR_INVALID: return "invalid argument";
+    case H2O_ERR_UNSUPPORTED: return "unsupported configuration";
+    case H2O_ERR_STATE: return "invalid call order or position overflow";
+    case H2O_ERR_OOM: return "out of device memory";
+    case H2O_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal launch interface between the C ABI (h2o_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h2o {
+
+struct DecodeArgs {
+  const void* q;       // [U, d]
+  const void* k_new;   // [U, d]
+  const void* v_new;   // [U, d]
+  void* k_slots;       // [U, k, d]
+  void* v_slots;       // [U, k, d]
+  float* score;        // [U, k]
+  int32_t* pos;        // [U, k]
+  float* out;          // [U, d]
+  int32_t* evicted;    // [U] or null
+  int32_t units;
+  int32_t k, r;
+  int32_t t;           // absolute position of the token being decoded
+  int32_t n_ring;      // live ring slots: min(t, r)
+  int32_t n_heavy;     // live heavy slots
+  float scale_log2;    // softmax scale * log2(e)
+};
+
+struct PrefillArgs {
+  const void* pq;      // prompt queries [U, P, d]
+  const void* pk;      // prompt keys    [U, P, d]
+  const void* pv;      // prompt values  [U, P, d]
+  void* k_slots;
+  void* v_slots;
+  float* score;
+  int32_t* pos;
+  float* row_max;      // scratch [U, P]: per query row, max logit (log2 domain)
+  float* row_inv;      // scratch [U, P]: per query row, 1 / sum of exp2(logit - max)
+  float* colsum;       // scratch [U, P]: accumulated attention per prompt position
+  int32_t units;
+  int32_t stride;      // scratch row stride in floats: max_prompt rounded up to 16
+  int32_t P;
+  int32_t k, r, h;
+  float scale_log2;
+};
+
+// dtype: 0 = float32, 1 = bfloat16.  Return hipSuccess or the launch error.
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int waves, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, hipStream_t s);
+
+// Automatic wavefronts per unit for the decode kernel.
+int decode_waves_auto(int units);
+
+}  // namespace h2o

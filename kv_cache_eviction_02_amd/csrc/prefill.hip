@@ -1,0 +1,363 @@
+// H2O prefill for gfx950: accumulated attention of every prompt position and the
+// initial choice of recent + heavy-hitter slots.
+//
+// Method (H2O summary "H2O: Heavy-Hitter Oracle for Efficient Generative
+// Inference", "Algorithm / figure walkthrough" step 1 and "The mechanism",
+// Heavy Hitters): the score of prompt position j is the column sum
+//   c_j = sum_{i >= j} softmax_i(scale * q_i . k_j),
+// the total causal attention it received from the prompt's own queries.  The
+// newest r positions are kept as the protected window; of the older ones the
+// h largest c_j are kept (ties keep the newer position); a prompt of at most
+// k = r + h positions is kept whole.
+//
+// Three kernels:
+//   rowstats : per query row i, m_i = max_j s_ij and 1 / sum_j exp2(s_ij - m_i)
+//              (s in the log2 domain), with S^T tiles on MFMA;
+//   colsum   : c_j = sum_i exp2(s_ij - m_i) / l_i, recomputing S tiles on MFMA;
+//              each wavefront owns 16 columns and walks the query tiles in a
+//              fixed order, so the sums are deterministic without atomics;
+//   select   : per unit, radix select of the h largest c_j among the older
+//              positions, then the gather of the kept K/V rows into slots.
+//
+// MFMA use: v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (f32).
+// Lane l supplies row l % 16 of a 16-row tile and the contiguous quarter
+// [(l / 16) * d / 4, (l / 16 + 1) * d / 4) of the head dimension; A and B use
+// the same split, so every product q_c * k_c is formed exactly once.  The
+// 16x16 result lands as acc[i] = dot(moving row 4 * (l / 16) + i, fixed row l % 16).
+#include <float.h>
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace h2o {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kTile = 16;
+
+template <typename T, int D>
+struct Frag {
+  static constexpr int kBytes = D / 4 * Elem<T>::kBytes;  // per lane: a quarter row
+  static constexpr int kChunks = kBytes / 16;
+  static_assert(kChunks * 16 == kBytes, "quarter row must be whole 16-byte chunks");
+  uint4 c[kChunks];
+
+  // Row `row0 + lane % 16` of a [n, D] matrix, quarter lane / 16; zero past n.
+  __device__ inline void load(const char* base, int row0, int n, int lane) {
+    const int row = row0 + (lane & 15);
+    const int quarter = lane >> 4;
+    if (row < n) {
+      const char* p = base + (size_t)row * (D * Elem<T>::kBytes) + quarter * kBytes;
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) c[i] = load16(p + 16 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) c[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+};
+
+// acc[i] = dot(moving row 4*(lane/16)+i, fixed row lane%16)
+template <typename T, int D>
+__device__ inline f32x4 tile_dot(const Frag<T, D>& mv, const Frag<T, D>& fx) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < Frag<T, D>::kChunks; ++i)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, mv.c[i]),
+                                                    __builtin_bit_cast(bf16x8, fx.c[i]), acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < Frag<T, D>::kChunks; ++i) {
+      const uint32_t a4[4] = {mv.c[i].x, mv.c[i].y, mv.c[i].z, mv.c[i].w};
+      const uint32_t b4[4] = {fx.c[i].x, fx.c[i].y, fx.c[i].z, fx.c[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a4[e]), __uint_as_float(b4[e]), acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
+// Blocks of one unit are kept on one XCD (blocks are dispatched round-robin over
+// the 8 XCDs), so a unit's Q and K tiles are shared through that XCD's L2.
+__device__ inline int xcd_local_block(int total) {
+  const int L = blockIdx.x;
+  if (total % 8 != 0) return L;
+  return (L % 8) * (total / 8) + L / 8;
+}
+
+constexpr int kWaves = 4;             // wavefronts per block, 16 rows each
+constexpr int kRowsPerBlock = kWaves * kTile;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kWaves * 64) void rowstats_kernel(PrefillArgs a, int stride, int nblk) {
+  const int id = xcd_local_block(nblk * a.units);
+  const int unit = id / nblk;
+  const int blk = nblk - 1 - id % nblk;  // longest rows first
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int P = a.P;
+  const int i0 = blk * kRowsPerBlock + wave * kTile;
+  if (i0 >= P) return;
+  constexpr int ROWB = D * Elem<T>::kBytes;
+  const char* Qb = (const char*)a.pq + (size_t)unit * P * ROWB;
+  const char* Kb = (const char*)a.pk + (size_t)unit * P * ROWB;
+
+  Frag<T, D> fq;
+  fq.load(Qb, i0, P, lane);
+  const int qi = i0 + (lane & 15);
+  const int g4 = (lane >> 4) * 4;
+  float m = -INFINITY, l = 0.f;
+  for (int j0 = 0; j0 <= i0; j0 += kTile) {
+    Frag<T, D> fk;
+    fk.load(Kb, j0, P, lane);
+    const f32x4 acc = tile_dot<T, D>(fk, fq);
+    float s[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kj = j0 + g4 + i;
+      s[i] = kj <= qi ? acc[i] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[i]);
+    }
+    const float mn = fmaxf(m, mx);
+    if (mn > -INFINITY) {
+      float add = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) add += fast_exp2(s[i] - mn);
+      l = l * fast_exp2(m - mn) + add;
+      m = mn;
+    }
+  }
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    const float mo = __shfl_xor(m, off, 64);
+    const float lo = __shfl_xor(l, off, 64);
+    const float mn = fmaxf(m, mo);
+    l = l * fast_exp2(m - mn) + lo * fast_exp2(mo - mn);
+    m = mn;
+  }
+  if (lane < 16 && qi < P) {
+    a.row_max[(size_t)unit * stride + qi] = m;
+    a.row_inv[(size_t)unit * stride + qi] = 1.f / l;
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kWaves * 64) void colsum_kernel(PrefillArgs a, int stride, int nblk) {
+  const int id = xcd_local_block(nblk * a.units);
+  const int unit = id / nblk;
+  const int blk = id % nblk;             // first columns have the most rows
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int P = a.P;
+  const int j0 = blk * kRowsPerBlock + wave * kTile;
+  if (j0 >= P) return;
+  constexpr int ROWB = D * Elem<T>::kBytes;
+  const char* Qb = (const char*)a.pq + (size_t)unit * P * ROWB;
+  const char* Kb = (const char*)a.pk + (size_t)unit * P * ROWB;
+  const float* rmax = a.row_max + (size_t)unit * stride;
+  const float* rinv = a.row_inv + (size_t)unit * stride;
+
+  Frag<T, D> fk;
+  fk.load(Kb, j0, P, lane);
+  const int kj = j0 + (lane & 15);
+  const int g4 = (lane >> 4) * 4;
+  float csum = 0.f;
+  for (int i0 = j0; i0 < P; i0 += kTile) {
+    Frag<T, D> fq;
+    fq.load(Qb, i0, P, lane);
+    const float4 mq = *reinterpret_cast<const float4*>(rmax + i0 + g4);
+    const float4 iq = *reinterpret_cast<const float4*>(rinv + i0 + g4);
+    const float mqa[4] = {mq.x, mq.y, mq.z, mq.w};
+    const float iqa[4] = {iq.x, iq.y, iq.z, iq.w};
+    const f32x4 acc = tile_dot<T, D>(fq, fk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qi = i0 + g4 + i;
+      const bool valid = qi < P && qi >= kj;
+      const float p = fast_exp2(acc[i] * a.scale_log2 - mqa[i]) * iqa[i];
+      csum += valid ? p : 0.f;
+    }
+  }
+  csum += __shfl_xor(csum, 16, 64);
+  csum += __shfl_xor(csum, 32, 64);
+  if (lane < 16 && kj < P) a.colsum[(size_t)unit * stride + kj] = csum;
+}
+
+constexpr int kSelThreads = 256;
+
+// Exclusive prefix sum over the block; returns the block total in *total.
+__device__ inline int block_exclusive_scan(int v, int* buf, int* total) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kSelThreads; off <<= 1) {
+    const int add = tid >= off ? buf[tid - off] : 0;
+    __syncthreads();
+    buf[tid] += add;
+    __syncthreads();
+  }
+  const int incl = buf[tid];
+  *total = buf[kSelThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs a, int stride) {
+  constexpr int ROWB = D * Elem<T>::kBytes;
+  constexpr int CH = ROWB / 16;  // 16-byte chunks per row
+  __shared__ int hist[256];
+  __shared__ int buf[kSelThreads];
+  __shared__ int s_slot[kSelThreads];
+  __shared__ int s_digit, s_need;
+
+  const int unit = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int P = a.P, r = a.r, h = a.h, k = a.k;
+  const float* c = a.colsum + (size_t)unit * stride;
+  const int n_ring = P < r ? P : r;
+  const int n_pool = P - n_ring;          // positions older than the window
+  const bool keep_all = n_pool <= h;
+  const int n_sel = keep_all ? n_pool : h;
+
+  const char* Kp = (const char*)a.pk + (size_t)unit * P * ROWB;
+  const char* Vp = (const char*)a.pv + (size_t)unit * P * ROWB;
+  char* Ks = (char*)a.k_slots + (size_t)unit * k * ROWB;
+  char* Vs = (char*)a.v_slots + (size_t)unit * k * ROWB;
+  float* score = a.score + (size_t)unit * k;
+  int32_t* pos = a.pos + (size_t)unit * k;
+
+  // Radix select (4 x 8 bits) of the h-th largest score bit pattern among the
+  // pool; scores are >= 0 so their bits order like the values.
+  uint32_t thr = 0;
+  int need = 0;
+  if (!keep_all && h > 0) {
+    uint32_t prefix = 0, mask = 0;
+    need = h;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      hist[tid] = 0;
+      __syncthreads();
+      for (int j = tid; j < n_pool; j += kSelThreads) {
+        const uint32_t b = __float_as_uint(c[j]);
+        if ((b & mask) == prefix) atomicAdd(&hist[(b >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int cum = 0;
+        for (int d = 255; d >= 0; --d) {
+          if (cum + hist[d] >= need) {
+            s_digit = d;
+            s_need = need - cum;
+            break;
+          }
+          cum += hist[d];
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_digit << shift;
+      mask |= 255u << shift;
+      need = s_need;
+      __syncthreads();
+    }
+    thr = prefix;
+  }
+
+  // Walk the pool from the newest position down: an equal-to-threshold score is
+  // taken while fewer than `need` newer equal ones were; selected positions get
+  // heavy slots in ascending position order.
+  int eq_seen = 0, sel_seen = 0;
+  for (int hi = n_pool; hi > 0; hi -= kSelThreads) {
+    const int p = hi - 1 - tid;
+    bool eq = false, gt = false;
+    if (p >= 0 && !keep_all && h > 0) {
+      const uint32_t b = __float_as_uint(c[p]);
+      eq = b == thr;
+      gt = b > thr;
+    }
+    int eq_total, sel_total;
+    const int eq_rank = eq_seen + block_exclusive_scan(eq ? 1 : 0, buf, &eq_total);
+    const bool sel = p >= 0 && (keep_all || gt || (eq && eq_rank < need));
+    const int sel_rank = sel_seen + block_exclusive_scan(sel ? 1 : 0, buf, &sel_total);
+    eq_seen += eq_total;
+    sel_seen += sel_total;
+    const int slot = sel ? r + (n_sel - 1 - sel_rank) : -1;
+    s_slot[tid] = slot;
+    if (sel) {
+      score[slot] = c[p];
+      pos[slot] = p;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < kSelThreads * CH; idx += kSelThreads) {
+      const int x = idx / CH, part = idx % CH;
+      const int sl = s_slot[x];
+      if (sl >= 0) {
+        const int pp = hi - 1 - x;
+        store16(Ks + (size_t)sl * ROWB + part * 16, load16(Kp + (size_t)pp * ROWB + part * 16));
+        store16(Vs + (size_t)sl * ROWB + part * 16, load16(Vp + (size_t)pp * ROWB + part * 16));
+      }
+    }
+    __syncthreads();
+  }
+
+  // Protected window: the newest n_ring prompt positions, slot = position % r.
+  for (int i = tid; i < n_ring; i += kSelThreads) {
+    const int p = P - n_ring + i;
+    score[p % r] = c[p];
+    pos[p % r] = p;
+  }
+  for (int idx = tid; idx < n_ring * CH; idx += kSelThreads) {
+    const int p = P - n_ring + idx / CH, part = idx % CH;
+    store16(Ks + (size_t)(p % r) * ROWB + part * 16, load16(Kp + (size_t)p * ROWB + part * 16));
+    store16(Vs + (size_t)(p % r) * ROWB + part * 16, load16(Vp + (size_t)p * ROWB + part * 16));
+  }
+  // Unused slots.
+  for (int s = tid; s < k; s += kSelThreads) {
+    const bool used = s < r ? s < n_ring : s < r + n_sel;
+    if (!used) {
+      score[s] = 0.f;
+      pos[s] = -1;
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_prefill_td(const PrefillArgs& a, int stride, hipStream_t s) {
+  const int nblk = (a.P + kRowsPerBlock - 1) / kRowsPerBlock;
+  const dim3 grid((unsigned)(nblk * a.units));
+  hipLaunchKernelGGL((rowstats_kernel<T, D>), grid, dim3(kWaves * 64), 0, s, a, stride, nblk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((colsum_kernel<T, D>), grid, dim3(kWaves * 64), 0, s, a, stride, nblk);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((select_gather_kernel<T, D>), dim3(a.units), dim3(kSelThreads), 0, s, a, stride);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_prefill_t(const PrefillArgs& a, int head_dim, int stride, hipStream_t s) {
+  switch (head_dim) {
+    case 64: return launch_prefill_td<T, 64>(a, stride, s);
+    case 96: return launch_prefill_td<T, 96>(a, stride, s);
+    case 128: return launch_prefill_td<T, 128>(a, stride, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, hipStream_t s) {
+  const int stride = a.stride;
+  if (dtype == 0) return launch_prefill_t<float>(a, head_dim, stride, s);
+  if (dtype == 1) return launch_prefill_t<bf16>(a, head_dim, stride, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace h2o
