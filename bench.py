@@ -196,8 +196,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--decode-waves", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-units-per-worker", type=int, default=16)
-    ap.add_argument("--cpu-steps", type=int, default=64)
+    ap.add_argument("--cpu-units-per-worker", type=int, default=32)
+    ap.add_argument("--cpu-steps", type=int, default=128)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

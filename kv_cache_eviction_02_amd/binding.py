@@ -143,6 +143,8 @@ class H2OCache:
         self.recent, self.heavy, self.k = recent, heavy, recent + heavy
         self.dtype = dtype
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         shape = (batch, heads, self.k, head_dim)
         if state is None:
             self.k_slots = torch.zeros(shape, dtype=dtype, device=self.device)

@@ -138,8 +138,10 @@ __global__ __launch_bounds__(kWaves * 64) void rowstats_kernel(PrefillArgs a, in
     const float mo = __shfl_xor(m, off, 64);
     const float lo = __shfl_xor(l, off, 64);
     const float mn = fmaxf(m, mo);
-    l = l * fast_exp2(m - mn) + lo * fast_exp2(mo - mn);
-    m = mn;
+    if (mn > -INFINITY) {  // both halves may still be empty for the first query rows
+      l = l * fast_exp2(m - mn) + lo * fast_exp2(mo - mn);
+      m = mn;
+    }
   }
   if (lane < 16 && qi < P) {
     a.row_max[(size_t)unit * stride + qi] = m;
