@@ -43,6 +43,14 @@ struct Elem<bf16> {
 };
 
 __device__ inline uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Streaming 16-byte load with the non-temporal hint: data read once per kernel
+// should not displace reusable lines from the caches.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline uint4 load16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ inline void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // DPP lane permutations (row = 16 lanes).

@@ -120,27 +120,28 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
 
-  for (int base = 0; base < n_att; base += NG * U) {
-    uint4 kr[U], vr[U];
-    int jj[U];
+  // Row batches of NG * U rows.  Loads are unconditional (rows past the end and
+  // idle lanes re-read a valid row and are masked out afterwards) so that the
+  // compiler can track outstanding loads exactly; the next batch is in flight
+  // while the current one is consumed.
+  constexpr int STEP = NG * U;
+  auto fetch = [&](int base, uint4 (&kr)[U], uint4 (&vr)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = base + u * NG + grp;
-      jj[u] = j;
-      kr[u] = make_uint4(0, 0, 0, 0);
-      vr[u] = make_uint4(0, 0, 0, 0);
-      if (act && j < n_att) {
-        const char* kp = kn;
-        const char* vp = vn;
-        if (j < n_live) {
-          const size_t off = (size_t)slot_of(j) * ROWB;
-          kp = Kb + off;
-          vp = Vb + off;
-        }
-        kr[u] = load16(kp + gl * 16);
-        vr[u] = load16(vp + gl * 16);
+      const char* kp = kn;
+      const char* vp = vn;
+      if (j < n_live) {
+        const size_t off = (size_t)slot_of(j) * ROWB;
+        kp = Kb + off;
+        vp = Vb + off;
       }
+      const int c = act ? gl : 0;
+      kr[u] = load16_stream(kp + c * 16);
+      vr[u] = load16_stream(vp + c * 16);
     }
+  };
+  auto consume = [&](int base, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
     float lg[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -148,9 +149,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       E::unpack(kr[u], kf);
       float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) d = fmaf(qf[e], kf[e], d);
+      for (int e = 0; e < EPL; ++e) d = fmaf(qf[e], kf[e], d);  // qf is 0 on idle lanes
       d = group_sum<G>(d);
-      const int j = jj[u];
+      const int j = base + u * NG + grp;
       lg[u] = j < n_att ? d * a.scale_log2 : -INFINITY;
       if (j < n_att) {
         if (gl == 0) s_logit[j] = lg[u];
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       for (int e = 0; e < EPL; ++e) o[e] *= alpha;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float p = fast_exp2(lg[u] - mn);
+        const float p = fast_exp2(lg[u] - mn);  // 0 for rows past the end
         float vf[EPL];
         E::unpack(vr[u], vf);
         lsum += p;
@@ -184,6 +185,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       }
       m = mn;
     }
+  };
+
+  uint4 ka[U], va[U], kb[U], vb[U];
+  fetch(0, ka, va);
+  for (int base = 0; base < n_att; base += 2 * STEP) {
+    fetch(base + STEP, kb, vb);
+    consume(base, ka, va);
+    fetch(base + 2 * STEP, ka, va);
+    consume(base + STEP, kb, vb);
   }
 
   // Merge the row groups: global max M, normaliser L, output.
@@ -300,7 +310,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
 template <typename T, int D, int NW>
 hipError_t launch_nw(const DecodeArgs& a, hipStream_t s) {
-  constexpr int U = NW <= 2 ? 4 : 2;
+  constexpr int U = 1;  // more loads in flight per wave measured slower at opt30b and neox20b
   const int n_live = a.n_ring + a.n_heavy;
   const size_t lds = (size_t)(n_live + 1) * sizeof(float);
   hipLaunchKernelGGL((decode_kernel<T, D, NW, U>), dim3(a.units), dim3(NW * 64), lds, s, a);
