@@ -147,6 +147,10 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0):
     cache = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy, wl.prompt, dtype,
                      wl.scale, device=dev, decode_waves=waves)
     stream = torch.cuda.current_stream()
+    # The first prefill also loads the kernels' code objects; the second one,
+    # which rebuilds the same state from the same prompt, is the one timed.
+    cache.prefill(*prompt)
+    torch.cuda.synchronize()
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     p0.record(stream)
     cache.prefill(*prompt)

@@ -90,7 +90,8 @@ typedef struct {
 } h2o_state;
 
 /* Create a context bound to a caller-owned state.  Allocates the prefill
- * scratch (column sums and row statistics, 3 * B * H * max_prompt floats) with
+ * scratch (row statistics and column sums, 2 * B * H * max_prompt floats,
+ * max_prompt rounded up to 16) with
  * hipMalloc on the current device; the state buffers are neither allocated nor
  * touched.  With start_live > 0 the ctx adopts the state already in the
  * buffers: it must satisfy min(start_pos, recent) <= start_live <= min(start_pos, k),

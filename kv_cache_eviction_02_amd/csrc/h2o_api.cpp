@@ -22,7 +22,7 @@ struct h2o_ctx {
   int32_t n_live;   // live slots per unit
   bool has_state;
   int32_t stride;   // scratch row stride (floats)
-  float* scratch;   // 3 * units * stride floats: row max, row inverse sum, column sums
+  float* scratch;   // 2 * units * stride floats: row log-sum-exp, column sums
 };
 
 namespace {
@@ -86,7 +86,7 @@ h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** o
   c->stride = (cfg->max_prompt + 15) / 16 * 16;
   c->scratch = nullptr;
   if (cfg->max_prompt > 0) {
-    const size_t bytes = (size_t)3 * units * c->stride * sizeof(float);
+    const size_t bytes = (size_t)2 * units * c->stride * sizeof(float);
     const hipError_t e = hipMalloc((void**)&c->scratch, bytes);
     if (e != hipSuccess) {
       delete c;
@@ -112,9 +112,8 @@ h2o_status h2o_prefill(h2o_ctx* ctx, const void* q, const void* k, const void* v
   a.v_slots = ctx->st.v_slots;
   a.score = ctx->st.score;
   a.pos = ctx->st.pos;
-  a.row_max = ctx->scratch;
-  a.row_inv = ctx->scratch + units * ctx->stride;
-  a.colsum = ctx->scratch + 2 * units * ctx->stride;
+  a.row_lse = ctx->scratch;
+  a.colsum = ctx->scratch + units * ctx->stride;
   a.units = (int32_t)units;
   a.stride = ctx->stride;
   a.P = prompt_len;

@@ -32,9 +32,8 @@ struct PrefillArgs {
   void* v_slots;
   float* score;
   int32_t* pos;
-  float* row_max;      // scratch [U, P]: per query row, max logit (log2 domain)
-  float* row_inv;      // scratch [U, P]: per query row, 1 / sum of exp2(logit - max)
-  float* colsum;       // scratch [U, P]: accumulated attention per prompt position
+  float* row_lse;      // scratch [U, stride]: per query row, log2 of the softmax denominator (log2 domain)
+  float* colsum;       // scratch [U, stride]: accumulated attention per prompt position
   int32_t units;
   int32_t stride;      // scratch row stride in floats: max_prompt rounded up to 16
   int32_t P;

@@ -11,11 +11,12 @@
 // k = r + h positions is kept whole.
 //
 // Three kernels:
-//   rowstats : per query row i, m_i = max_j s_ij and 1 / sum_j exp2(s_ij - m_i)
-//              (s in the log2 domain), with S^T tiles on MFMA;
-//   colsum   : c_j = sum_i exp2(s_ij - m_i) / l_i, recomputing S tiles on MFMA;
-//              each wavefront owns 16 columns and walks the query tiles in a
-//              fixed order, so the sums are deterministic without atomics;
+//   rowstats : per query row i, lse_i = m_i + log2(sum_j exp2(s_ij - m_i)) with
+//              s in the log2 domain, from S^T tiles on MFMA;
+//   colsum   : c_j = sum_i exp2(s_ij - lse_i), recomputing the S tiles on MFMA;
+//              each wavefront owns 64 columns (32 for f32) and walks the query
+//              tiles in a fixed order, so the sums are deterministic without
+//              atomics;
 //   select   : per unit, radix select of the h largest c_j among the older
 //              positions, then the gather of the kept K/V rows into slots.
 //
@@ -90,105 +91,176 @@ __device__ inline int xcd_local_block(int total) {
   return (L % 8) * (total / 8) + L / 8;
 }
 
-constexpr int kWaves = 4;             // wavefronts per block, 16 rows each
-constexpr int kRowsPerBlock = kWaves * kTile;
+constexpr int kWaves = 4;  // wavefronts per block, each with its own rows
 
+// Fixed 16-row subtiles held by one wavefront (B operands): 64 rows for bf16,
+// 32 for f32 (whose fragments are twice as large).
+template <typename T>
+constexpr int kFixed = sizeof(T) == 2 ? 4 : 2;
+
+template <typename T>
+constexpr int rows_per_wave() { return kFixed<T> * kTile; }
+
+// Row statistics: lse_i = m_i + log2(sum_{j <= i} exp2(s_ij - m_i)), with
+// s = scale*log2(e) * q_i . k_j.  A wavefront owns kFixed*16 queries and walks
+// the key subtiles up to its last query, the next subtile in flight while the
+// current one is multiplied.
 template <typename T, int D>
 __global__ __launch_bounds__(kWaves * 64) void rowstats_kernel(PrefillArgs a, int stride, int nblk) {
+  constexpr int QS = kFixed<T>;
+  constexpr int ROWS = rows_per_wave<T>();
   const int id = xcd_local_block(nblk * a.units);
   const int unit = id / nblk;
   const int blk = nblk - 1 - id % nblk;  // longest rows first
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int P = a.P;
-  const int i0 = blk * kRowsPerBlock + wave * kTile;
+  const int i0 = (blk * kWaves + wave) * ROWS;
   if (i0 >= P) return;
   constexpr int ROWB = D * Elem<T>::kBytes;
   const char* Qb = (const char*)a.pq + (size_t)unit * P * ROWB;
   const char* Kb = (const char*)a.pk + (size_t)unit * P * ROWB;
 
-  Frag<T, D> fq;
-  fq.load(Qb, i0, P, lane);
-  const int qi = i0 + (lane & 15);
-  const int g4 = (lane >> 4) * 4;
-  float m = -INFINITY, l = 0.f;
-  for (int j0 = 0; j0 <= i0; j0 += kTile) {
-    Frag<T, D> fk;
-    fk.load(Kb, j0, P, lane);
-    const f32x4 acc = tile_dot<T, D>(fk, fq);
-    float s[4];
-    float mx = -INFINITY;
+  Frag<T, D> fq[QS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kj = j0 + g4 + i;
-      s[i] = kj <= qi ? acc[i] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s[i]);
-    }
-    const float mn = fmaxf(m, mx);
-    if (mn > -INFINITY) {
+  for (int q = 0; q < QS; ++q) fq[q].load(Qb, i0 + q * kTile, P, lane);
+  const int g4 = (lane >> 4) * 4;
+  float m[QS], l[QS];
+#pragma unroll
+  for (int q = 0; q < QS; ++q) {
+    m[q] = -INFINITY;
+    l[q] = 0.f;
+  }
+  const int kend = min(P, i0 + ROWS);  // keys past the wave's last query are masked anyway
+  const int nkt = (kend + kTile - 1) / kTile;
+
+  auto step = [&](int kt, const Frag<T, D>& fk) {
+    const int j0 = kt * kTile;
+    const bool diag = j0 + kTile - 1 > i0;  // uniform: some key may follow some query
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      const f32x4 acc = tile_dot<T, D>(fk, fq[q]);
+      const int qi = i0 + q * kTile + (lane & 15);
+      float s[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] = acc[i] * a.scale_log2;
+        if (diag) s[i] = j0 + g4 + i <= qi ? s[i] : -INFINITY;
+        mx = fmaxf(mx, s[i]);
+      }
+      const float mn = fmaxf(m[q], mx);
+      const float base = mn == -INFINITY ? 0.f : mn;  // nothing seen yet: keep l = 0
       float add = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) add += fast_exp2(s[i] - mn);
-      l = l * fast_exp2(m - mn) + add;
-      m = mn;
+      for (int i = 0; i < 4; ++i) add += fast_exp2(s[i] - base);
+      l[q] = l[q] * fast_exp2(m[q] - base) + add;
+      m[q] = mn;
+    }
+  };
+
+  Frag<T, D> fa, fb;
+  fa.load(Kb, 0, P, lane);
+  for (int kt = 0; kt < nkt; kt += 2) {
+    if (kt + 1 < nkt) fb.load(Kb, (kt + 1) * kTile, P, lane);
+    step(kt, fa);
+    if (kt + 1 < nkt) {
+      if (kt + 2 < nkt) fa.load(Kb, (kt + 2) * kTile, P, lane);
+      step(kt + 1, fb);
     }
   }
+  // Merge the four lane groups holding the same queries.
 #pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-    const float mo = __shfl_xor(m, off, 64);
-    const float lo = __shfl_xor(l, off, 64);
-    const float mn = fmaxf(m, mo);
-    if (mn > -INFINITY) {  // both halves may still be empty for the first query rows
-      l = l * fast_exp2(m - mn) + lo * fast_exp2(mo - mn);
-      m = mn;
+  for (int q = 0; q < QS; ++q) {
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float mo = __shfl_xor(m[q], off, 64);
+      const float lo = __shfl_xor(l[q], off, 64);
+      const float mn = fmaxf(m[q], mo);
+      const float base = mn == -INFINITY ? 0.f : mn;
+      l[q] = l[q] * fast_exp2(m[q] - base) + lo * fast_exp2(mo - base);
+      m[q] = mn;
     }
-  }
-  if (lane < 16 && qi < P) {
-    a.row_max[(size_t)unit * stride + qi] = m;
-    a.row_inv[(size_t)unit * stride + qi] = 1.f / l;
+    const int qi = i0 + q * kTile + lane;
+    if (lane < 16 && qi < P) a.row_lse[(size_t)unit * stride + qi] = m[q] + __log2f(l[q]);
   }
 }
 
+// Column sums c_j = sum_{i >= j} exp2(s_ij - lse_i).  A wavefront owns
+// kFixed*16 keys and walks the query subtiles from its first key to the end
+// of the prompt in a fixed order, so the sums are deterministic.
 template <typename T, int D>
 __global__ __launch_bounds__(kWaves * 64) void colsum_kernel(PrefillArgs a, int stride, int nblk) {
+  constexpr int QS = kFixed<T>;
+  constexpr int ROWS = rows_per_wave<T>();
   const int id = xcd_local_block(nblk * a.units);
   const int unit = id / nblk;
-  const int blk = id % nblk;             // first columns have the most rows
+  const int blk = id % nblk;  // first columns have the most rows
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int P = a.P;
-  const int j0 = blk * kRowsPerBlock + wave * kTile;
+  const int j0 = (blk * kWaves + wave) * ROWS;
   if (j0 >= P) return;
   constexpr int ROWB = D * Elem<T>::kBytes;
   const char* Qb = (const char*)a.pq + (size_t)unit * P * ROWB;
   const char* Kb = (const char*)a.pk + (size_t)unit * P * ROWB;
-  const float* rmax = a.row_max + (size_t)unit * stride;
-  const float* rinv = a.row_inv + (size_t)unit * stride;
+  const float* lse = a.row_lse + (size_t)unit * stride;
 
-  Frag<T, D> fk;
-  fk.load(Kb, j0, P, lane);
-  const int kj = j0 + (lane & 15);
-  const int g4 = (lane >> 4) * 4;
-  float csum = 0.f;
-  for (int i0 = j0; i0 < P; i0 += kTile) {
-    Frag<T, D> fq;
-    fq.load(Qb, i0, P, lane);
-    const float4 mq = *reinterpret_cast<const float4*>(rmax + i0 + g4);
-    const float4 iq = *reinterpret_cast<const float4*>(rinv + i0 + g4);
-    const float mqa[4] = {mq.x, mq.y, mq.z, mq.w};
-    const float iqa[4] = {iq.x, iq.y, iq.z, iq.w};
-    const f32x4 acc = tile_dot<T, D>(fq, fk);
+  Frag<T, D> fk[QS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int qi = i0 + g4 + i;
-      const bool valid = qi < P && qi >= kj;
-      const float p = fast_exp2(acc[i] * a.scale_log2 - mqa[i]) * iqa[i];
-      csum += valid ? p : 0.f;
+  for (int q = 0; q < QS; ++q) fk[q].load(Kb, j0 + q * kTile, P, lane);
+  const int g4 = (lane >> 4) * 4;
+  float cs[QS];
+#pragma unroll
+  for (int q = 0; q < QS; ++q) cs[q] = 0.f;
+  const int qt0 = j0 / kTile;
+  const int nqt = (P + kTile - 1) / kTile;
+
+  auto step = [&](int qt, const Frag<T, D>& fq, const float4& lq) {
+    const int i0 = qt * kTile;
+    const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
+    const bool edge = i0 < j0 + ROWS - 1 || i0 + kTile > P;  // uniform: masking needed
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      const f32x4 acc = tile_dot<T, D>(fq, fk[q]);
+      const int kj = j0 + q * kTile + (lane & 15);
+      float add = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(fmaf(acc[i], a.scale_log2, -lv[i]));
+        const int qi = i0 + g4 + i;
+        add += (!edge || (qi >= kj && qi < P)) ? p : 0.f;
+      }
+      cs[q] += add;
+    }
+  };
+
+  Frag<T, D> fa, fb;
+  float4 la, lb;
+  fa.load(Qb, qt0 * kTile, P, lane);
+  la = *reinterpret_cast<const float4*>(lse + qt0 * kTile + g4);
+  for (int qt = qt0; qt < nqt; qt += 2) {
+    if (qt + 1 < nqt) {
+      fb.load(Qb, (qt + 1) * kTile, P, lane);
+      lb = *reinterpret_cast<const float4*>(lse + (qt + 1) * kTile + g4);
+    }
+    step(qt, fa, la);
+    if (qt + 1 < nqt) {
+      if (qt + 2 < nqt) {
+        fa.load(Qb, (qt + 2) * kTile, P, lane);
+        la = *reinterpret_cast<const float4*>(lse + (qt + 2) * kTile + g4);
+      }
+      step(qt + 1, fb, lb);
     }
   }
-  csum += __shfl_xor(csum, 16, 64);
-  csum += __shfl_xor(csum, 32, 64);
-  if (lane < 16 && kj < P) a.colsum[(size_t)unit * stride + kj] = csum;
+#pragma unroll
+  for (int q = 0; q < QS; ++q) {
+    float c = cs[q];
+    c += __shfl_xor(c, 16, 64);
+    c += __shfl_xor(c, 32, 64);
+    const int kj = j0 + q * kTile + lane;
+    if (lane < 16 && kj < P) a.colsum[(size_t)unit * stride + kj] = c;
+  }
 }
 
 constexpr int kSelThreads = 256;
@@ -331,7 +403,8 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs 
 
 template <typename T, int D>
 hipError_t launch_prefill_td(const PrefillArgs& a, int stride, hipStream_t s) {
-  const int nblk = (a.P + kRowsPerBlock - 1) / kRowsPerBlock;
+  constexpr int rows_per_block = kWaves * rows_per_wave<T>();
+  const int nblk = (a.P + rows_per_block - 1) / rows_per_block;
   const dim3 grid((unsigned)(nblk * a.units));
   hipLaunchKernelGGL((rowstats_kernel<T, D>), grid, dim3(kWaves * 64), 0, s, a, stride, nblk);
   hipError_t e = hipGetLastError();
