@@ -79,7 +79,10 @@ typedef struct {
   float scale;         /* softmax scale; 0 selects 1/sqrt(head_dim) */
   int32_t start_pos;   /* adopt an existing state: position of the next token to decode */
   int32_t start_live;  /* adopt an existing state: number of live slots (0 = no state yet) */
-  int32_t decode_waves;/* wavefronts per (batch, head) unit in the decode kernel: 0 = automatic, else 1, 2, 4 or 8 */
+  int32_t decode_waves;/* wavefronts per decode workgroup: 0 = automatic, else 1, 2, 4 or 8 */
+  int32_t decode_split;/* decode workgroups per (batch, head) unit: 0 = automatic, 1 = one,
+                          2..64 = that many (each streams a share of the rows; for batches
+                          with few units) */
 } h2o_config;
 
 typedef struct {
@@ -91,7 +94,9 @@ typedef struct {
 
 /* Create a context bound to a caller-owned state.  Allocates the prefill
  * scratch (row statistics and column sums, 2 * B * H * max_prompt floats,
- * max_prompt rounded up to 16) with
+ * max_prompt rounded up to 16) and, when the decode is split over S > 1
+ * workgroups per unit, the split scratch (B * H * (S * (d + 2) + k + 1)
+ * floats and B * H arrival counters, zeroed here) with
  * hipMalloc on the current device; the state buffers are neither allocated nor
  * touched.  With start_live > 0 the ctx adopts the state already in the
  * buffers: it must satisfy min(start_pos, recent) <= start_live <= min(start_pos, k),
@@ -119,6 +124,20 @@ h2o_status h2o_prefill(h2o_ctx* ctx, const void* q, const void* k, const void* v
  * when t would exceed INT32_MAX - 1. */
 h2o_status h2o_decode_step(h2o_ctx* ctx, const void* q, const void* k_new, const void* v_new,
                            float* out, int32_t* evicted_pos, void* stream);
+
+/* n_steps consecutive decode steps over tokens known in advance, as when a
+ * long stream is fed through the cache (summary, "Algorithm / figure
+ * walkthrough", step 5; "Results and evidence", long streams).  Identical in
+ * effect to n_steps calls of h2o_decode_step with the step-s slices
+ * q[s], k_new[s], v_new[s] -> out[s], evicted_pos[s], without a host round
+ * trip per step.  q, k_new, v_new: [n_steps, B, H, d] kv_dtype; out:
+ * [n_steps, B, H, d] float32; evicted_pos: [n_steps, B, H] int32 or NULL.
+ * n_steps >= 1 and t + n_steps must stay below INT32_MAX - 1, else
+ * H2O_ERR_INVALID / H2O_ERR_STATE before anything is enqueued.  n_steps
+ * kernels on `stream`; allocates nothing.  On a launch error the counters
+ * reflect the steps that were enqueued. */
+h2o_status h2o_decode_steps(h2o_ctx* ctx, int32_t n_steps, const void* q, const void* k_new,
+                            const void* v_new, float* out, int32_t* evicted_pos, void* stream);
 
 /* Host-side counters: position of the next token to decode and number of live
  * slots per unit (the same for every unit).  Either pointer may be NULL. */

@@ -38,6 +38,7 @@ class h2o_config(ctypes.Structure):
         ("start_pos", ctypes.c_int32),
         ("start_live", ctypes.c_int32),
         ("decode_waves", ctypes.c_int32),
+        ("decode_split", ctypes.c_int32),
     ]
 
 
@@ -75,6 +76,8 @@ def load_library(path=LIB_PATH):
     lib.h2o_prefill.restype = ctypes.c_int
     lib.h2o_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.h2o_decode_step.restype = ctypes.c_int
+    lib.h2o_decode_steps.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
+    lib.h2o_decode_steps.restype = ctypes.c_int
     lib.h2o_query.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.h2o_query.restype = ctypes.c_int
     lib.h2o_destroy.argtypes = [vp]
@@ -111,6 +114,10 @@ def h2o_decode_step(ctx, q, k_new, v_new, out, evicted_pos, stream):
     return load_library().h2o_decode_step(ctx, q, k_new, v_new, out, evicted_pos, stream)
 
 
+def h2o_decode_steps(ctx, n_steps, q, k_new, v_new, out, evicted_pos, stream):
+    return load_library().h2o_decode_steps(ctx, n_steps, q, k_new, v_new, out, evicted_pos, stream)
+
+
 def h2o_query(ctx):
     t, n = ctypes.c_int32(), ctypes.c_int32()
     st = load_library().h2o_query(ctx, ctypes.byref(t), ctypes.byref(n))
@@ -133,7 +140,7 @@ class H2OCache:
 
     def __init__(self, batch, heads, head_dim, recent, heavy, max_prompt, dtype,
                  scale=0.0, device="cuda", decode_waves=0, start_pos=0, start_live=0,
-                 state=None):
+                 state=None, decode_split=0):
         import torch
         self.torch = torch
         load_library()
@@ -159,7 +166,7 @@ class H2OCache:
                 raise ValueError("state tensors must be contiguous, on the device, with the right dtypes")
         self.cfg = h2o_config(batch, heads, head_dim, recent, heavy, max_prompt,
                               H2O_F32 if dtype == torch.float32 else H2O_BF16, scale,
-                              start_pos, start_live, decode_waves)
+                              start_pos, start_live, decode_waves, decode_split)
         self.state = h2o_state(self.k_slots.data_ptr(), self.v_slots.data_ptr(),
                                self.score.data_ptr(), self.pos.data_ptr())
         st, ctx = h2o_create(self.cfg, self.state)
@@ -192,6 +199,21 @@ class H2OCache:
         evicted = self.evicted if evicted is None else evicted
         _check(h2o_decode_step(self.ctx, *ptrs, out.data_ptr(), evicted.data_ptr(), self._stream()),
                "h2o_decode_step")
+        return out, evicted
+
+    def steps(self, q, k_new, v_new, out=None, evicted=None):
+        """n consecutive decode steps over known tokens: inputs [n, B, H, d];
+        returns (out [n, B, H, d] float32, evicted [n, B, H] int32)."""
+        n = q.shape[0]
+        shape = (n, self.batch, self.heads, self.head_dim)
+        ptrs = [self._input(x, shape, nm) for x, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"))]
+        torch = self.torch
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        if evicted is None:
+            evicted = torch.empty(shape[:3], dtype=torch.int32, device=self.device)
+        _check(h2o_decode_steps(self.ctx, n, *ptrs, out.data_ptr(), evicted.data_ptr(), self._stream()),
+               "h2o_decode_steps")
         return out, evicted
 
     def position(self):

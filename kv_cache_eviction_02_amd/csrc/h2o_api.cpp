@@ -23,6 +23,8 @@ struct h2o_ctx {
   bool has_state;
   int32_t stride;   // scratch row stride (floats)
   float* scratch;   // 2 * units * stride floats: row log-sum-exp, column sums
+  h2o::SplitScratch split;  // split decode scratch (split.splits < 2: unused)
+  void* split_mem;
 };
 
 namespace {
@@ -34,7 +36,8 @@ bool valid_dims(const h2o_config* c) {
          c->max_prompt >= 0 && (c->kv_dtype == H2O_F32 || c->kv_dtype == H2O_BF16) &&
          isfinite(c->scale) && c->scale >= 0.f && c->start_pos >= 0 && c->start_live >= 0 &&
          (c->decode_waves == 0 || c->decode_waves == 1 || c->decode_waves == 2 ||
-          c->decode_waves == 4 || c->decode_waves == 8);
+          c->decode_waves == 4 || c->decode_waves == 8) &&
+         c->decode_split >= 0 && c->decode_split <= 64;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -85,6 +88,9 @@ h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** o
   c->has_state = n0 > 0;
   c->stride = (cfg->max_prompt + 15) / 16 * 16;
   c->scratch = nullptr;
+  c->split_mem = nullptr;
+  c->split = h2o::SplitScratch{nullptr, nullptr, nullptr, 1};
+  const int splits = cfg->decode_split ? cfg->decode_split : h2o::decode_split_auto((int)units, c->waves);
   if (cfg->max_prompt > 0) {
     const size_t bytes = (size_t)2 * units * c->stride * sizeof(float);
     const hipError_t e = hipMalloc((void**)&c->scratch, bytes);
@@ -92,6 +98,23 @@ h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** o
       delete c;
       return from_hip(e);
     }
+  }
+  if (splits > 1) {
+    const size_t n_part = (size_t)units * splits * (cfg->head_dim + 2);
+    const size_t n_logit = (size_t)units * (k + 1);
+    const size_t bytes = (n_part + n_logit) * sizeof(float) + (size_t)units * sizeof(unsigned);
+    hipError_t e = hipMalloc(&c->split_mem, bytes);
+    if (e == hipSuccess) e = hipMemset(c->split_mem, 0, bytes);
+    if (e != hipSuccess) {
+      if (c->split_mem) (void)hipFree(c->split_mem);
+      if (c->scratch) (void)hipFree(c->scratch);
+      delete c;
+      return from_hip(e);
+    }
+    c->split.partials = (float*)c->split_mem;
+    c->split.logits = c->split.partials + n_part;
+    c->split.counters = (unsigned*)(c->split.logits + n_logit);
+    c->split.splits = splits;
   }
   *out = c;
   return H2O_OK;
@@ -130,14 +153,13 @@ h2o_status h2o_prefill(h2o_ctx* ctx, const void* q, const void* k, const void* v
   return H2O_OK;
 }
 
-h2o_status h2o_decode_step(h2o_ctx* ctx, const void* q, const void* k_new, const void* v_new,
-                           float* out, int32_t* evicted_pos, void* stream) {
-  if (!ctx || !q || !k_new || !v_new || !out) return H2O_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) ||
-      ((uintptr_t)evicted_pos & 3u) != 0)
-    return H2O_ERR_INVALID;
-  if (!ctx->has_state) return H2O_ERR_STATE;
-  if (ctx->t >= INT32_MAX - 1) return H2O_ERR_STATE;
+}  // extern "C"
+
+namespace {
+
+// Enqueue one decode step at the ctx's current position and advance it.
+h2o_status enqueue_step(h2o_ctx* ctx, const void* q, const void* k_new, const void* v_new,
+                        float* out, int32_t* evicted_pos, hipStream_t stream) {
   const int32_t r = ctx->cfg.recent;
   const int32_t n_ring = ctx->t < r ? ctx->t : r;
   h2o::DecodeArgs a;
@@ -158,10 +180,46 @@ h2o_status h2o_decode_step(h2o_ctx* ctx, const void* q, const void* k_new, const
   a.n_heavy = ctx->n_live - n_ring;
   a.scale_log2 = ctx->scale_log2;
   const hipError_t e = h2o::launch_decode(a, ctx->cfg.kv_dtype, ctx->cfg.head_dim, ctx->waves,
-                                          (hipStream_t)stream);
+                                          &ctx->split, stream);
   if (e != hipSuccess) return from_hip(e);
   ctx->t += 1;
   if (ctx->n_live < ctx->k) ctx->n_live += 1;
+  return H2O_OK;
+}
+
+bool step_args_ok(const void* q, const void* k_new, const void* v_new, const float* out,
+                  const int32_t* evicted_pos) {
+  return q && k_new && v_new && out && aligned16(q) && aligned16(k_new) && aligned16(v_new) &&
+         aligned16(out) && ((uintptr_t)evicted_pos & 3u) == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+h2o_status h2o_decode_step(h2o_ctx* ctx, const void* q, const void* k_new, const void* v_new,
+                           float* out, int32_t* evicted_pos, void* stream) {
+  if (!ctx || !step_args_ok(q, k_new, v_new, out, evicted_pos)) return H2O_ERR_INVALID;
+  if (!ctx->has_state) return H2O_ERR_STATE;
+  if (ctx->t >= INT32_MAX - 1) return H2O_ERR_STATE;
+  return enqueue_step(ctx, q, k_new, v_new, out, evicted_pos, (hipStream_t)stream);
+}
+
+h2o_status h2o_decode_steps(h2o_ctx* ctx, int32_t n_steps, const void* q, const void* k_new,
+                            const void* v_new, float* out, int32_t* evicted_pos, void* stream) {
+  if (!ctx || n_steps < 1 || !step_args_ok(q, k_new, v_new, out, evicted_pos)) return H2O_ERR_INVALID;
+  if (!ctx->has_state) return H2O_ERR_STATE;
+  if ((int64_t)ctx->t + n_steps >= INT32_MAX - 1) return H2O_ERR_STATE;
+  const size_t units = (size_t)ctx->cfg.batch * ctx->cfg.heads;
+  const size_t in_step = units * ctx->cfg.head_dim * (ctx->cfg.kv_dtype == H2O_BF16 ? 2 : 4);
+  const size_t out_step = units * ctx->cfg.head_dim;
+  for (int32_t s = 0; s < n_steps; ++s) {
+    const h2o_status st = enqueue_step(
+        ctx, (const char*)q + s * in_step, (const char*)k_new + s * in_step,
+        (const char*)v_new + s * in_step, out + s * out_step,
+        evicted_pos ? evicted_pos + s * units : nullptr, (hipStream_t)stream);
+    if (st != H2O_OK) return st;
+  }
   return H2O_OK;
 }
 
@@ -176,6 +234,10 @@ h2o_status h2o_destroy(h2o_ctx* ctx) {
   if (!ctx) return H2O_OK;
   hipError_t e = hipSuccess;
   if (ctx->scratch) e = hipFree(ctx->scratch);
+  if (ctx->split_mem) {
+    const hipError_t e2 = hipFree(ctx->split_mem);
+    if (e == hipSuccess) e = e2;
+  }
   delete ctx;
   return from_hip(e);
 }

@@ -24,6 +24,14 @@ struct DecodeArgs {
   float scale_log2;    // softmax scale * log2(e)
 };
 
+// Scratch of the split decode (several workgroups per unit).
+struct SplitScratch {
+  float* partials;     // [U, S, d + 2]: max, sum, output of each workgroup's rows
+  float* logits;       // [U, k + 1]
+  unsigned* counters;  // [U]: arrivals in the current step, zero between launches
+  int32_t splits;      // S >= 2
+};
+
 struct PrefillArgs {
   const void* pq;      // prompt queries [U, P, d]
   const void* pk;      // prompt keys    [U, P, d]
@@ -42,10 +50,14 @@ struct PrefillArgs {
 };
 
 // dtype: 0 = float32, 1 = bfloat16.  Return hipSuccess or the launch error.
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int waves, hipStream_t s);
+// sp == nullptr or sp->splits < 2: one workgroup per unit.
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int waves,
+                         const SplitScratch* sp, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, hipStream_t s);
 
 // Automatic wavefronts per unit for the decode kernel.
 int decode_waves_auto(int units);
+// Automatic workgroups per unit (1 = no split).
+int decode_split_auto(int units, int waves);
 
 }  // namespace h2o

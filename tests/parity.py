@@ -68,7 +68,7 @@ def torch_dtype(wl):
 class Harness:
     """Runs one workload on the GPU and checks sampled units against the oracle."""
 
-    def __init__(self, wl, units, steps, device="cuda", decode_waves=0):
+    def __init__(self, wl, units, steps, device="cuda", decode_waves=0, decode_split=0):
         self.wl = wl
         self.units = units
         self.steps = steps
@@ -78,7 +78,7 @@ class Harness:
         self.idx = torch.tensor(units, dtype=torch.long, device=device)
         self.cache = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy,
                               max_prompt=wl.prompt, dtype=torch_dtype(wl), scale=wl.scale,
-                              device=device, decode_waves=decode_waves)
+                              device=device, decode_waves=decode_waves, decode_split=decode_split)
         self.flat = dict(pos=self.cache.pos.view(U, k), score=self.cache.score.view(U, k),
                          k=self.cache.k_slots.view(U, k, -1), v=self.cache.v_slots.view(U, k, -1))
         # exact input values and storage bits of the sampled units, all positions used

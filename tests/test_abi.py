@@ -24,7 +24,8 @@ def header_functions():
 
 def cfg(**kw):
     base = dict(batch=2, heads=3, head_dim=64, recent=4, heavy=4, max_prompt=0,
-                kv_dtype=B.H2O_BF16, scale=0.0, start_pos=0, start_live=0, decode_waves=0)
+                kv_dtype=B.H2O_BF16, scale=0.0, start_pos=0, start_live=0, decode_waves=0,
+                decode_split=0)
     base.update(kw)
     return B.h2o_config(**base)
 
@@ -36,8 +37,8 @@ def state(k=FAKE, v=FAKE, s=FAKE, p=FAKE):
 def test_library_exports_every_header_function():
     lib = B.load_library()
     names = header_functions()
-    assert names == sorted(["h2o_create", "h2o_prefill", "h2o_decode_step", "h2o_query",
-                            "h2o_destroy", "h2o_status_string"])
+    assert names == sorted(["h2o_create", "h2o_prefill", "h2o_decode_step", "h2o_decode_steps",
+                            "h2o_query", "h2o_destroy", "h2o_status_string"])
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -53,8 +54,9 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stdio.h>
 #include "h2o.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu\n", sizeof(h2o_config), offsetof(h2o_config, scale),
-         offsetof(h2o_config, decode_waves), sizeof(h2o_state), offsetof(h2o_state, pos));
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(h2o_config), offsetof(h2o_config, scale),
+         offsetof(h2o_config, decode_waves), sizeof(h2o_state), offsetof(h2o_state, pos),
+         offsetof(h2o_config, decode_split));
   printf("%d\n", H2O_MAX_K);
   return 0;
 }''')
@@ -64,7 +66,7 @@ int main(void) {
     got = list(map(int, lines[0].split()))
     assert got == [ctypes.sizeof(B.h2o_config), B.h2o_config.scale.offset,
                    B.h2o_config.decode_waves.offset, ctypes.sizeof(B.h2o_state),
-                   B.h2o_state.pos.offset]
+                   B.h2o_state.pos.offset, B.h2o_config.decode_split.offset]
     assert int(lines[1]) == B.H2O_MAX_K
 
 
@@ -84,6 +86,8 @@ def test_status_strings():
     (dict(scale=-1.0), B.H2O_ERR_INVALID),
     (dict(scale=float("nan")), B.H2O_ERR_INVALID),
     (dict(decode_waves=3), B.H2O_ERR_INVALID),
+    (dict(decode_split=-1), B.H2O_ERR_INVALID),
+    (dict(decode_split=65), B.H2O_ERR_INVALID),
     (dict(head_dim=80), B.H2O_ERR_UNSUPPORTED),
     (dict(head_dim=256), B.H2O_ERR_UNSUPPORTED),
     (dict(recent=4096, heavy=4097), B.H2O_ERR_UNSUPPORTED),
@@ -123,6 +127,8 @@ def test_call_order_and_argument_checks_without_device_work():
         assert k2.h2o_prefill(ctx, FAKE, FAKE, FAKE, 1, None) == B.H2O_ERR_INVALID
         assert k2.h2o_prefill(ctx, FAKE, FAKE, FAKE, 0, None) == B.H2O_ERR_INVALID
         assert k2.h2o_prefill(ctx, 0, FAKE, FAKE, 1, None) == B.H2O_ERR_INVALID
+        assert k2.h2o_decode_steps(ctx, 4, FAKE, FAKE, FAKE, FAKE, None, None) == B.H2O_ERR_STATE
+        assert k2.h2o_decode_steps(ctx, 0, FAKE, FAKE, FAKE, FAKE, None, None) == B.H2O_ERR_INVALID
         assert k2.h2o_query(ctx) == (B.H2O_OK, 0, 0)   # unchanged by failed calls
     finally:
         assert k2.h2o_destroy(ctx) == B.H2O_OK
@@ -157,4 +163,12 @@ def test_misaligned_pointers_are_rejected():
     assert k2.h2o_decode_step(ctx, FAKE + 4, FAKE, FAKE, FAKE, None, None) == B.H2O_ERR_INVALID
     assert k2.h2o_decode_step(ctx, FAKE, FAKE, FAKE, FAKE, FAKE + 2, None) == B.H2O_ERR_INVALID
     assert k2.h2o_query(ctx) == (B.H2O_OK, 10, 8)
+    k2.h2o_destroy(ctx)
+
+
+def test_decode_steps_position_overflow_is_rejected_up_front():
+    st, ctx = k2.h2o_create(cfg(start_pos=INT32_MAX - 10, start_live=8), state())
+    assert st == B.H2O_OK
+    assert k2.h2o_decode_steps(ctx, 9, FAKE, FAKE, FAKE, FAKE, None, None) == B.H2O_ERR_STATE
+    assert k2.h2o_query(ctx) == (B.H2O_OK, INT32_MAX - 10, 8)
     k2.h2o_destroy(ctx)

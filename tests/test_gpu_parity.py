@@ -34,13 +34,13 @@ def _need_gpu():
     torch.cuda.synchronize()
 
 
-def run_workload(wl, n_units, steps, check_every=1, decode_waves=0, kv_every=64):
+def run_workload(wl, n_units, steps, check_every=1, decode_waves=0, kv_every=64, decode_split=0):
     from parity import Harness, sample_units
     units = sample_units(wl, n_units)
     say(f"[parity] {wl.name} B={wl.batch} H={wl.heads} d={wl.head_dim} P={wl.prompt} "
         f"k={wl.k} ({wl.recent}+{wl.heavy}) {wl.kv_dtype} steps={steps} units={units[:6]}... "
-        f"waves={decode_waves}")
-    hn = Harness(wl, units, steps, decode_waves=decode_waves)
+        f"waves={decode_waves} split={decode_split}")
+    hn = Harness(wl, units, steps, decode_waves=decode_waves, decode_split=decode_split)
     try:
         hn.prefill()
         stats = hn.run(check_every=check_every, kv_every=kv_every)
@@ -104,6 +104,18 @@ def test_decode_wave_counts(waves):
     run_workload(wl, 8, 40, decode_waves=waves, kv_every=8)
 
 
+@pytest.mark.parametrize("split,waves", [(2, 4), (8, 1), (8, 4), (16, 2), (64, 1)])
+def test_split_decode_long_stream(split, waves):
+    """Several workgroups per unit, partials combined by the last to arrive."""
+    run_workload(WORKLOADS["llama7b_stream"], 4, 600, check_every=3, decode_waves=waves,
+                 decode_split=split, kv_every=100)
+
+
+def test_split_decode_tiny_and_opt67b():
+    run_workload(WORKLOADS["tiny_fp32"], 2, 64, decode_split=4, decode_waves=1, kv_every=1)
+    run_workload(WORKLOADS["opt6.7b"], 8, 64, decode_split=3, decode_waves=2, kv_every=8)
+
+
 # ---- edge cases ----------------------------------------------------------------------
 
 EDGE = [
@@ -124,20 +136,21 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("split", [1, 5])
 @pytest.mark.parametrize("wl", EDGE, ids=lambda w: w.name)
-def test_edge_cases(wl):
-    stats = run_workload(wl, wl.units, wl.steps, kv_every=1)
+def test_edge_cases(wl, split):
+    stats = run_workload(wl, wl.units, wl.steps, kv_every=1, decode_split=split)
     if wl.k >= wl.n_positions:
         assert stats.near_ties == 0
 
 
-@pytest.mark.parametrize("waves", [1, 0])
-def test_large_budget(waves):
+@pytest.mark.parametrize("waves,split", [(1, 1), (0, 1), (1, 4)])
+def test_large_budget(waves, split):
     """k = 2524: more slots than the decode kernel's per-thread prefetch covers
     with one wavefront, and a prompt of 3000 for the selection kernel."""
     wl = Workload(107, "large_budget_bf16", 1, 2, 128, 3000, 20, 1024, 1500, "bf16", "zipf",
                   zipf_alpha=1.1)
-    run_workload(wl, 2, 20, decode_waves=waves, kv_every=5)
+    run_workload(wl, 2, 20, decode_waves=waves, decode_split=split, kv_every=5)
 
 
 # ---- exact ties ------------------------------------------------------------------------
@@ -242,3 +255,38 @@ def test_run_twice_bitwise_identical():
     for a, b in zip(*snaps):
         assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
                            b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+@pytest.mark.parametrize("name", ["opt6.7b", "llama7b_stream"])
+def test_decode_steps_equals_single_steps(name):
+    """h2o_decode_steps over n known tokens gives bit-identical outputs,
+    evictions and state to n h2o_decode_step calls."""
+    from kv_cache_eviction_02_amd import H2OCache
+    wl = WORKLOADS[name]
+    n = 96
+    say(f"[parity] decode_steps vs decode_step: {name}, {n} steps")
+    prompt = stage_prompt(wl, "cuda")
+    dq, dk, dv = stage_decode(wl, 0, n, "cuda")
+    res = []
+    for multi in (False, True):
+        cache = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy, wl.prompt,
+                         torch.bfloat16, wl.scale)
+        cache.prefill(*prompt)
+        if multi:
+            out, ev = cache.steps(dq[:40], dk[:40], dv[:40])
+            out2, ev2 = cache.steps(dq[40:], dk[40:], dv[40:])
+            out, ev = torch.cat([out, out2]), torch.cat([ev, ev2])
+        else:
+            outs, evs = [], []
+            for s in range(n):
+                o, e = cache.step(dq[s], dk[s], dv[s])
+                outs.append(o.clone())
+                evs.append(e.clone())
+            out, ev = torch.stack(outs), torch.stack(evs)
+        torch.cuda.synchronize()
+        assert cache.position() == (wl.prompt + n, wl.k)
+        res.append([out, ev, cache.k_slots.view(torch.int16).clone(),
+                    cache.v_slots.view(torch.int16).clone(), cache.score.clone(), cache.pos.clone()])
+        cache.close()
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
