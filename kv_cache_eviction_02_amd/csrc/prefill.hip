@@ -104,11 +104,13 @@ constexpr int rows_per_wave() { return kFixed<T> * kTile; }
 // Row statistics: lse_i = m_i + log2(sum_{j <= i} exp2(s_ij - m_i)), with
 // s = scale*log2(e) * q_i . k_j.  A wavefront owns kFixed*16 queries and walks
 // the key subtiles up to its last query, the next subtile in flight while the
-// current one is multiplied.
+// current one is multiplied; the running max is rescaled once per pair of
+// subtiles, and the scale is folded into the exp2 argument.
 template <typename T, int D>
 __global__ __launch_bounds__(kWaves * 64) void rowstats_kernel(PrefillArgs a, int stride, int nblk) {
   constexpr int QS = kFixed<T>;
   constexpr int ROWS = rows_per_wave<T>();
+  constexpr float kLow = -1.0e30f;  // finite start for the running max: no inf - inf
   const int id = xcd_local_block(nblk * a.units);
   const int unit = id / nblk;
   const int blk = nblk - 1 - id % nblk;  // longest rows first
@@ -120,6 +122,7 @@ __global__ __launch_bounds__(kWaves * 64) void rowstats_kernel(PrefillArgs a, in
   constexpr int ROWB = D * Elem<T>::kBytes;
   const char* Qb = (const char*)a.pq + (size_t)unit * P * ROWB;
   const char* Kb = (const char*)a.pk + (size_t)unit * P * ROWB;
+  const float sc = a.scale_log2;
 
   Frag<T, D> fq[QS];
 #pragma unroll
@@ -128,46 +131,54 @@ __global__ __launch_bounds__(kWaves * 64) void rowstats_kernel(PrefillArgs a, in
   float m[QS], l[QS];
 #pragma unroll
   for (int q = 0; q < QS; ++q) {
-    m[q] = -INFINITY;
+    m[q] = kLow;
     l[q] = 0.f;
   }
   const int kend = min(P, i0 + ROWS);  // keys past the wave's last query are masked anyway
   const int nkt = (kend + kTile - 1) / kTile;
 
-  auto step = [&](int kt, const Frag<T, D>& fk) {
+  // Raw products of one key subtile against every fixed subtile, masked to
+  // -inf where the key follows the query or does not exist.
+  auto mult = [&](int kt, const Frag<T, D>& fk, f32x4 (&acc)[QS]) {
     const int j0 = kt * kTile;
-    const bool diag = j0 + kTile - 1 > i0;  // uniform: some key may follow some query
+    const bool diag = j0 + kTile - 1 > i0;  // uniform
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
-      const f32x4 acc = tile_dot<T, D>(fk, fq[q]);
-      const int qi = i0 + q * kTile + (lane & 15);
-      float s[4];
-      float mx = -INFINITY;
+      acc[q] = tile_dot<T, D>(fk, fq[q]);
+      if (diag || kt >= nkt) {
+        const int qi = i0 + q * kTile + (lane & 15);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[i] = acc[i] * a.scale_log2;
-        if (diag) s[i] = j0 + g4 + i <= qi ? s[i] : -INFINITY;
-        mx = fmaxf(mx, s[i]);
+        for (int i = 0; i < 4; ++i)
+          acc[q][i] = (kt < nkt && j0 + g4 + i <= qi) ? acc[q][i] : -INFINITY;
       }
-      const float mn = fmaxf(m[q], mx);
-      const float base = mn == -INFINITY ? 0.f : mn;  // nothing seen yet: keep l = 0
+    }
+  };
+  auto update = [&](const f32x4 (&x)[QS], const f32x4 (&y)[QS]) {
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      float mx = fmaxf(fmaxf(x[q][0], x[q][1]), fmaxf(x[q][2], x[q][3]));
+      mx = fmaxf(mx, fmaxf(fmaxf(y[q][0], y[q][1]), fmaxf(y[q][2], y[q][3])));
+      const float mn = fmaxf(m[q], mx * sc);
       float add = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) add += fast_exp2(s[i] - base);
-      l[q] = l[q] * fast_exp2(m[q] - base) + add;
+      for (int i = 0; i < 4; ++i) {
+        add += fast_exp2(fmaf(x[q][i], sc, -mn));
+        add += fast_exp2(fmaf(y[q][i], sc, -mn));
+      }
+      l[q] = fmaf(l[q], fast_exp2(m[q] - mn), add);
       m[q] = mn;
     }
   };
 
   Frag<T, D> fa, fb;
+  f32x4 ax[QS], ay[QS];
   fa.load(Kb, 0, P, lane);
   for (int kt = 0; kt < nkt; kt += 2) {
-    if (kt + 1 < nkt) fb.load(Kb, (kt + 1) * kTile, P, lane);
-    step(kt, fa);
-    if (kt + 1 < nkt) {
-      if (kt + 2 < nkt) fa.load(Kb, (kt + 2) * kTile, P, lane);
-      step(kt + 1, fb);
-    }
+    fb.load(Kb, (kt + 1) * kTile, P, lane);  // zero rows past the prompt
+    mult(kt, fa, ax);
+    if (kt + 2 < nkt) fa.load(Kb, (kt + 2) * kTile, P, lane);
+    mult(kt + 1, fb, ay);
+    update(ax, ay);
   }
   // Merge the four lane groups holding the same queries.
 #pragma unroll
@@ -177,8 +188,7 @@ __global__ __launch_bounds__(kWaves * 64) void rowstats_kernel(PrefillArgs a, in
       const float mo = __shfl_xor(m[q], off, 64);
       const float lo = __shfl_xor(l[q], off, 64);
       const float mn = fmaxf(m[q], mo);
-      const float base = mn == -INFINITY ? 0.f : mn;
-      l[q] = l[q] * fast_exp2(m[q] - base) + lo * fast_exp2(mo - base);
+      l[q] = l[q] * fast_exp2(m[q] - mn) + lo * fast_exp2(mo - mn);
       m[q] = mn;
     }
     const int qi = i0 + q * kTile + lane;
