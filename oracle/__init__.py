@@ -11,4 +11,8 @@ from .h2o_ref import (  # noqa: F401
     decode_step,
     run_trace,
     members_from_slots,
+    e4m3_value,
+    e4m3_encode,
+    quantize_row_e4m3,
+    dequantize_row_e4m3,
 )

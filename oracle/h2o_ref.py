@@ -91,13 +91,16 @@ def prefill(Q, K, recent, heavy, scale):
     return {j: float(c[j]) for j in prefill_keep(c, recent, heavy)}, c
 
 
-def decode_step(members, t, q, K, V, recent, heavy, scale):
+def decode_step(members, t, q, K, V, recent, heavy, scale, K_cached=None, V_cached=None):
     """One H2O decode step for the token at absolute position t.
 
     ``members`` maps each cached position (< t) to its accumulated score.  K and
     V are indexable by absolute position and hold rows for every member and for
-    t itself.  Returns StepResult(out, evicted, members after the step, the
-    softmax weight of each attended position, attended positions in order).
+    t itself.  When the cache stores rows in a lossy form, K_cached / V_cached
+    give the rows as stored (indexable by position) and are used for the
+    members; the token being decoded always attends with its exact row.
+    Returns StepResult(out, evicted, members after the step, the softmax weight
+    of each attended position, attended positions in order).
 
     Order of work (summary, "Algorithm / figure walkthrough", steps 2-4):
       1. attend over the members and the new token;
@@ -108,8 +111,10 @@ def decode_step(members, t, q, K, V, recent, heavy, scale):
     """
     q = np.asarray(q, dtype=np.float64)
     attended = sorted(members) + [t]
-    Ka = np.asarray([K[j] for j in attended], dtype=np.float64)
-    Va = np.asarray([V[j] for j in attended], dtype=np.float64)
+    Kc = K if K_cached is None else K_cached
+    Vc = V if V_cached is None else V_cached
+    Ka = np.asarray([Kc[j] for j in attended[:-1]] + [K[t]], dtype=np.float64)
+    Va = np.asarray([Vc[j] for j in attended[:-1]] + [V[t]], dtype=np.float64)
     logits = scale * (Ka @ q)
     w = np.exp(logits - logits.max())
     p = w / w.sum()
@@ -127,17 +132,25 @@ def decode_step(members, t, q, K, V, recent, heavy, scale):
     return StepResult(out, evicted, after, weights, attended)
 
 
-def run_trace(Q, K, V, prompt, steps, recent, heavy, scale):
+def run_trace(Q, K, V, prompt, steps, recent, heavy, scale, cache="exact"):
     """Prefill on positions [0, prompt) then ``steps`` decode steps.
 
-    Q, K, V hold rows for positions [0, prompt + steps).  Returns
-    (members after prefill, prompt column sums, [StepResult per step])."""
+    Q, K, V hold rows for positions [0, prompt + steps).  cache="e4m3" stores
+    every cached row as per-row-scaled E4M3 (quantize_row_e4m3); the prefill
+    scores still come from the exact prompt.  Returns (members after prefill,
+    prompt column sums, [StepResult per step])."""
     members, c = prefill(Q[:prompt], K[:prompt], recent, heavy, scale)
+    Kc = Vc = None
+    if cache == "e4m3":
+        Kc = np.asarray([dequantize_row_e4m3(*quantize_row_e4m3(row)) for row in K])
+        Vc = np.asarray([dequantize_row_e4m3(*quantize_row_e4m3(row)) for row in V])
+    elif cache != "exact":
+        raise ValueError(cache)
     seeded = dict(members)
     results = []
     for s in range(steps):
         t = prompt + s
-        res = decode_step(members, t, Q[t], K, V, recent, heavy, scale)
+        res = decode_step(members, t, Q[t], K, V, recent, heavy, scale, Kc, Vc)
         results.append(res)
         members = res.members
     return seeded, c, results
@@ -149,3 +162,68 @@ def members_from_slots(pos, score):
     score = np.asarray(score, dtype=np.float64)
     live = pos >= 0
     return {int(p): float(s) for p, s in zip(pos[live], score[live])}
+
+
+# ---- E4M3 cache rows ------------------------------------------------------------
+#
+# OCP 8-bit floating point, E4M3 variant without infinities: sign, 4 exponent
+# bits with bias 7, 3 mantissa bits; exponent 0 holds subnormals (m/8 * 2^-6);
+# 0x7F / 0xFF are NaN, so the largest finite magnitude is 448.  Conversion
+# rounds to nearest with ties to the even mantissa.  A cached row x is stored
+# as codes of x * (448 / amax) with amax = max |x|, and the per-row scale
+# amax / 448; both quotients are float32 (the precision the kernel decides the
+# codes in).  A row of zeros is stored as zero codes with scale 0.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(codes):
+    """float64 value of E4M3 codes (NaN for the two NaN codes)."""
+    codes = np.asarray(codes, dtype=np.int64)
+    sign = np.where(codes & 0x80, -1.0, 1.0)
+    e = (codes >> 3) & 0xF
+    m = codes & 7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+def e4m3_encode(y):
+    """Round float values to E4M3 codes (nearest, ties to even).
+
+    Values up to the midpoint between 448 and the next step of the grid (464)
+    round to 448; a row scaled by the float32 quotient 448 / amax can exceed 448
+    by an ulp."""
+    y = np.asarray(y, dtype=np.float64)
+    if np.any(np.abs(y) >= 464.0):
+        raise ValueError("value outside the E4M3 range")
+    sign = np.signbit(y).astype(np.int64) << 7
+    a = np.abs(y)
+    codes = np.empty(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # subnormal range: multiples of 2^-9; a result of 8 is the smallest normal, code 8
+    codes[sub] = np.rint(a[sub] / 2.0 ** -9).astype(np.int64)
+    an = a[~sub]
+    e = np.floor(np.log2(an)).astype(np.int64)
+    q = np.rint(an / np.exp2(e - 3.0)).astype(np.int64)   # 8 .. 16
+    carry = q == 16
+    e = e + carry
+    q = np.where(carry, 8, q)
+    codes[~sub] = ((e + 7) << 3) | (q - 8)
+    return (codes | sign).astype(np.uint8)
+
+
+def quantize_row_e4m3(x):
+    """One cached row -> (E4M3 codes, float32 scale)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x)))
+    if amax == 0:
+        return np.zeros(x.shape, dtype=np.uint8), np.float32(0.0)
+    inv = np.float32(E4M3_MAX) / amax
+    s = amax / np.float32(E4M3_MAX)
+    return e4m3_encode((x * inv).astype(np.float32)), np.float32(s)
+
+
+def dequantize_row_e4m3(codes, s):
+    """Exact float64 value of a stored row: code value times the row scale."""
+    return e4m3_value(codes) * np.float64(s)

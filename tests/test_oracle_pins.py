@@ -324,3 +324,74 @@ def test_tiny_trace_matches_recorded_trajectory():
         assert sorted(seeded) == u["prefill_kept"]
         assert [s.evicted for s in steps] == u["evicted"]
         assert sorted(steps[-1].members) == u["final_members"]
+
+
+# --- E4M3 cache rows -------------------------------------------------------------
+
+def test_e4m3_encode_matches_torch_float8_e4m3fn():
+    from oracle import e4m3_encode, e4m3_value
+    finite = [c for c in range(256) if not np.isnan(e4m3_value(c))]
+    vals = e4m3_value(finite)
+    order = np.argsort(vals)
+    sv = vals[order]
+    mids = (sv[:-1] + sv[1:]) / 2            # exact midpoints: ties to even
+    rng = np.random.default_rng(4)
+    x = np.concatenate([rng.uniform(-448, 448, 20000), rng.normal(0, 1, 20000),
+                        rng.normal(0, 0.004, 5000), mids, sv,
+                        [448.00003, -448.00003, 463.9]]).astype(np.float32)
+    ours = e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_e4m3_round_trip_and_row_quantization_bounds():
+    from oracle import dequantize_row_e4m3, e4m3_encode, e4m3_value, quantize_row_e4m3
+    for c in range(256):
+        v = e4m3_value(c)
+        if not np.isnan(v):
+            assert e4m3_encode(np.float32(v)) == c
+    rng = np.random.default_rng(8)
+    for trial in range(200):
+        x = (rng.standard_normal(128) * rng.uniform(1e-3, 50)).astype(np.float32)
+        codes, s = quantize_row_e4m3(x)
+        deq = dequantize_row_e4m3(codes, s)
+        amax = np.abs(x).max()
+        assert abs(abs(deq[np.argmax(np.abs(x))]) - amax) <= amax * 1e-6   # the peak maps to +-448
+        # half a quantum of the code grid, in row units
+        bound = np.maximum(np.abs(x) * 2.0 ** -4, s * 2.0 ** -10) * (1 + 1e-6)
+        assert np.all(np.abs(deq - x) <= bound)
+    codes, s = quantize_row_e4m3(np.zeros(8, dtype=np.float32))
+    assert s == 0 and not codes.any()
+
+
+def test_e4m3_cache_equals_exact_cache_when_rows_are_representable():
+    """Rows already on their own E4M3 grid are stored exactly, so the trace with
+    an E4M3 cache equals the exact one (checks the cached-row plumbing)."""
+    from oracle import e4m3_value
+    rng = np.random.default_rng(12)
+    P, T, r, h, d = 24, 20, 4, 6, 16
+    N = P + T
+    finite = np.array([c for c in range(256) if not np.isnan(e4m3_value(c))])
+    def grid_rows():
+        rows = e4m3_value(rng.choice(finite, size=(N, d)))
+        rows[:, 0] = 448.0                        # peak sets the row scale to exactly 1
+        return rows * 2.0 ** -6                   # power-of-two scale keeps the grid
+    Q = rng.standard_normal((N, d))
+    K, V = grid_rows(), grid_rows()
+    scale = 1 / np.sqrt(d)
+    _, _, exact = run_trace(Q, K, V, P, T, r, h, scale)
+    _, _, quant = run_trace(Q, K, V, P, T, r, h, scale, cache="e4m3")
+    for a, b in zip(exact, quant):
+        assert a.evicted == b.evicted
+        np.testing.assert_array_equal(a.out, b.out)
+
+
+def test_e4m3_cache_keeps_definition_4_3():
+    wl, Q, K, V = c1_unit(0)
+    seeded, _, steps = run_trace(Q, K, V, wl.prompt, wl.steps, wl.recent, wl.heavy, wl.scale,
+                                 cache="e4m3")
+    prev = set(seeded)
+    for s, res in enumerate(steps):
+        cur = set(res.members)
+        assert len(cur) == wl.k and len(cur - prev) <= 1
+        prev = cur
