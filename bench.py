@@ -36,11 +36,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DECODE_SOURCES = ["kv_cache_eviction_02_amd/csrc/decode.hip", "kv_cache_eviction_02_amd/csrc/common.h"]
 
 
-def alg_bytes_per_step(wl):
+def alg_bytes_per_step(wl, cache="input"):
     """Bytes one decode step must move at minimum: every live K and V row, the
     score read and write, q/k/v of the new token, the fp32 output, one admitted
-    row (K, V, score, position) and the evicted position."""
+    row (K, V, score, position) and the evicted position.  An E4M3 cache stores
+    one byte per element plus a float32 scale per K row and per V row."""
     U, k, d, e = wl.units, wl.k, wl.head_dim, wl.elem_bytes
+    if cache == "e4m3":
+        return (U * k * (d * 2 + 8) + U * k * 8 + U * 3 * d * e + U * d * 4
+                + U * (2 * d + 8 + 8) + U * 4)
     return (U * k * d * e * 2 + U * k * 8 + U * 3 * d * e + U * d * 4
             + U * (2 * d * e + 8) + U * 4)
 
@@ -128,7 +132,7 @@ def cpu_baseline(wl, units_per_worker, steps):
 
 # ---- GPU -----------------------------------------------------------------------
 
-def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0):
+def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, cache="input"):
     import torch
     from kv_cache_eviction_02_amd import H2OCache
     from kv_cache_eviction_02_amd.binding import load_library
@@ -145,7 +149,7 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0):
     print(f"[bench] staged inputs in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     cache = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy, wl.prompt, dtype,
-                     wl.scale, device=dev, decode_waves=waves, decode_split=split)
+                     wl.scale, device=dev, decode_waves=waves, decode_split=split, cache=cache)
     stream = torch.cuda.current_stream()
     # The first prefill also loads the kernels' code objects; the second one,
     # which rebuilds the same state from the same prompt, is the one timed.
@@ -210,6 +214,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=24)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--decode-waves", type=int, default=0)
+    ap.add_argument("--cache", default="input", choices=["input", "e4m3"],
+                    help="cache rows as the input dtype, or E4M3 codes with per-row scales")
     ap.add_argument("--decode-split", type=int, default=0,
                     help="decode workgroups per (batch, head) unit; 0 = library default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -240,14 +246,16 @@ def main():
         cpu = cpu_baseline(wl, args.cpu_units_per_worker, min(args.cpu_steps, wl.steps))
         print(f"[bench] cpu baseline done in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
+    if args.cache == "e4m3" and wl.kv_dtype != "bf16":
+        sys.exit("an E4M3 cache takes bf16 inputs")
     g = run_gpu(wl, steps, warmup, args.decode_waves, args.copy_calibration_mib, args.single_step_calls,
-                args.decode_split)
+                args.decode_split, args.cache)
     ms_per_step = g["region_ms"] / steps
     # one decode launch per step: the mean launch duration over the timed region
     mean_launch_ms = ms_per_step
-    bytes_step = alg_bytes_per_step(wl)
+    bytes_step = alg_bytes_per_step(wl, args.cache)
     achieved = bytes_step / (mean_launch_ms * 1e-3) / 1e9
-    traffic = traffic_for(wl.name, g["waves"])
+    traffic = traffic_for(wl.name, g["waves"]) if args.cache == "input" else None
     line = {
         "metric": METRIC,
         "value": 1e3 / ms_per_step,
@@ -259,12 +267,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.kv_dtype,
+        "dtype": wl.kv_dtype if args.cache == "input" else "bf16 in, e4m3 cache",
         "data": "synthetic",
         "config": {
             "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "head_dim": wl.head_dim,
             "prompt": wl.prompt, "k": wl.k, "recent": wl.recent, "heavy": wl.heavy,
-            "kv_dtype": wl.kv_dtype, "decode_waves": g["waves"], "decode_split": args.decode_split or "auto",
+            "kv_dtype": wl.kv_dtype, "cache": args.cache, "decode_waves": g["waves"],
+            "decode_split": args.decode_split or "auto",
             "parallelism": "none",
             "launch": "h2o_decode_step per step" if args.single_step_calls else "h2o_decode_steps",
         },

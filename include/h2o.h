@@ -64,6 +64,16 @@ typedef enum {
 
 typedef enum { H2O_F32 = 0, H2O_BF16 = 1 } h2o_dtype;
 
+/* How the cache stores K/V rows.  H2O_CACHE_INPUT: in kv_dtype, exact copies of
+ * the input rows.  H2O_CACHE_E4M3 (kv_dtype must be H2O_BF16): OCP E4M3 codes
+ * (bias 7, largest 448, round to nearest even) of x * (448 / amax) with the
+ * row scale amax / 448 in float32, amax = max |x| over the row (both
+ * quotients correctly rounded in float32; a zero row has zero codes and scale
+ * 0).  This composes the cache with quantization (summary, "What to notice
+ * when reading": H2O composes with quantization).  The prefill scores and the
+ * decoded token's own attention use the exact bf16 rows. */
+typedef enum { H2O_CACHE_INPUT = 0, H2O_CACHE_E4M3 = 1 } h2o_cache_dtype;
+
 /* Largest budget k = recent + heavy the decode kernel accepts (its per-row
  * logits live in LDS). */
 #define H2O_MAX_K 8192
@@ -83,13 +93,16 @@ typedef struct {
   int32_t decode_split;/* decode workgroups per (batch, head) unit: 0 = automatic, 1 = one,
                           2..64 = that many (each streams a share of the rows; for batches
                           with few units) */
+  int32_t cache_dtype; /* h2o_cache_dtype */
 } h2o_config;
 
 typedef struct {
-  void* k_slots;       /* [B, H, k, d] kv_dtype, device */
-  void* v_slots;       /* [B, H, k, d] kv_dtype, device */
+  void* k_slots;       /* [B, H, k, d] kv_dtype, or uint8 E4M3 codes; device */
+  void* v_slots;       /* [B, H, k, d] likewise */
   float* score;        /* [B, H, k] float32, device */
   int32_t* pos;        /* [B, H, k] int32, device */
+  float* k_scale;      /* [B, H, k] float32 row scales, device (E4M3 cache; else may be NULL) */
+  float* v_scale;      /* [B, H, k] float32 row scales, device (E4M3 cache; else may be NULL) */
 } h2o_state;
 
 /* Create a context bound to a caller-owned state.  Allocates the prefill

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(PKG, "libh2o.so")
 
 H2O_OK, H2O_ERR_INVALID, H2O_ERR_UNSUPPORTED, H2O_ERR_STATE, H2O_ERR_OOM, H2O_ERR_HIP = range(6)
 H2O_F32, H2O_BF16 = 0, 1
+H2O_CACHE_INPUT, H2O_CACHE_E4M3 = 0, 1
 H2O_MAX_K = 8192
 
 STATUS_NAMES = {
@@ -39,6 +40,7 @@ class h2o_config(ctypes.Structure):
         ("start_live", ctypes.c_int32),
         ("decode_waves", ctypes.c_int32),
         ("decode_split", ctypes.c_int32),
+        ("cache_dtype", ctypes.c_int32),
     ]
 
 
@@ -48,6 +50,8 @@ class h2o_state(ctypes.Structure):
         ("v_slots", ctypes.c_void_p),
         ("score", ctypes.c_void_p),
         ("pos", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -140,35 +144,50 @@ class H2OCache:
 
     def __init__(self, batch, heads, head_dim, recent, heavy, max_prompt, dtype,
                  scale=0.0, device="cuda", decode_waves=0, start_pos=0, start_live=0,
-                 state=None, decode_split=0):
+                 state=None, decode_split=0, cache="input"):
         import torch
         self.torch = torch
         load_library()
         if dtype not in (torch.float32, torch.bfloat16):
             raise ValueError("dtype must be torch.float32 or torch.bfloat16")
+        if cache not in ("input", "e4m3"):
+            raise ValueError("cache must be 'input' or 'e4m3'")
         self.batch, self.heads, self.head_dim = batch, heads, head_dim
         self.recent, self.heavy, self.k = recent, heavy, recent + heavy
         self.dtype = dtype
+        self.cache = cache
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
         shape = (batch, heads, self.k, head_dim)
+        slot_dtype = torch.uint8 if cache == "e4m3" else dtype
         if state is None:
-            self.k_slots = torch.zeros(shape, dtype=dtype, device=self.device)
-            self.v_slots = torch.zeros(shape, dtype=dtype, device=self.device)
+            self.k_slots = torch.zeros(shape, dtype=slot_dtype, device=self.device)
+            self.v_slots = torch.zeros(shape, dtype=slot_dtype, device=self.device)
             self.score = torch.zeros(shape[:3], dtype=torch.float32, device=self.device)
             self.pos = torch.full(shape[:3], -1, dtype=torch.int32, device=self.device)
+            self.k_scale = self.v_scale = None
+            if cache == "e4m3":
+                self.k_scale = torch.zeros(shape[:3], dtype=torch.float32, device=self.device)
+                self.v_scale = torch.zeros(shape[:3], dtype=torch.float32, device=self.device)
         else:
-            self.k_slots, self.v_slots, self.score, self.pos = state
-        for t_, dt in ((self.k_slots, dtype), (self.v_slots, dtype),
-                       (self.score, torch.float32), (self.pos, torch.int32)):
-            if t_.dtype != dt or not t_.is_contiguous() or t_.device != self.device:
+            self.k_slots, self.v_slots, self.score, self.pos = state[:4]
+            self.k_scale, self.v_scale = (state[4], state[5]) if len(state) > 4 else (None, None)
+        checks = [(self.k_slots, slot_dtype), (self.v_slots, slot_dtype),
+                  (self.score, torch.float32), (self.pos, torch.int32)]
+        if cache == "e4m3":
+            checks += [(self.k_scale, torch.float32), (self.v_scale, torch.float32)]
+        for t_, dt in checks:
+            if t_ is None or t_.dtype != dt or not t_.is_contiguous() or t_.device != self.device:
                 raise ValueError("state tensors must be contiguous, on the device, with the right dtypes")
         self.cfg = h2o_config(batch, heads, head_dim, recent, heavy, max_prompt,
                               H2O_F32 if dtype == torch.float32 else H2O_BF16, scale,
-                              start_pos, start_live, decode_waves, decode_split)
+                              start_pos, start_live, decode_waves, decode_split,
+                              H2O_CACHE_E4M3 if cache == "e4m3" else H2O_CACHE_INPUT)
         self.state = h2o_state(self.k_slots.data_ptr(), self.v_slots.data_ptr(),
-                               self.score.data_ptr(), self.pos.data_ptr())
+                               self.score.data_ptr(), self.pos.data_ptr(),
+                               self.k_scale.data_ptr() if self.k_scale is not None else None,
+                               self.v_scale.data_ptr() if self.v_scale is not None else None)
         st, ctx = h2o_create(self.cfg, self.state)
         _check(st, "h2o_create")
         self.ctx = ctx

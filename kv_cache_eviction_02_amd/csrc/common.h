@@ -42,6 +42,44 @@ struct Elem<bf16> {
   }
 };
 
+// Storage tag for E4M3 cache codes (OCP 8-bit float: bias 7, max 448, no inf).
+struct e4m3 {
+  uint8_t bits;
+};
+
+template <>
+struct Elem<e4m3> {
+  static constexpr int kPer16B = 16;
+  static constexpr int kBytes = 1;
+  // 16 codes -> 16 floats (exact); byte 0 of word i is element 4i.
+  __device__ static inline void unpack(const uint4& raw, float* x) {
+    typedef __attribute__((ext_vector_type(2))) float f2;
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+      const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+      x[4 * i] = lo.x;
+      x[4 * i + 1] = lo.y;
+      x[4 * i + 2] = hi.x;
+      x[4 * i + 3] = hi.y;
+    }
+  }
+};
+
+// Four floats already scaled into [-464, 464) -> four E4M3 codes, nearest
+// even.  Values in (448, 464) round to 448 under that rule; clamping them
+// first gives the same code on every path.
+__device__ inline uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f);
+  d = fminf(fmaxf(d, -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
 __device__ inline uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // Streaming 16-byte load with the non-temporal hint: data read once per kernel
@@ -75,6 +113,28 @@ __device__ inline float group_sum(float x) {
   if constexpr (G >= 32) x += __shfl_xor(x, 16, 64);
   if constexpr (G >= 64) x += __shfl_xor(x, 32, 64);
   return x;
+}
+
+// Maximum over aligned groups of G consecutive lanes (G <= 16).
+template <int G>
+__device__ inline float group_max(float x) {
+  static_assert(G == 4 || G == 8 || G == 16, "group size");
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  if constexpr (G >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  if constexpr (G >= 16) x = fmaxf(x, dpp<kDppRowMirror>(x));
+  return x;
+}
+
+// One E4M3 cache row chunk: 16 input values of a row whose absolute maximum
+// over all its lanes is amax -> 16 codes; the row scale is amax / 448.
+__device__ inline uint4 quantize16_e4m3(const float* x, float amax) {
+  const float inv = amax > 0.f ? __fdiv_rn(448.f, amax) : 0.f;
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = pack4_e4m3(x[4 * i] * inv, x[4 * i + 1] * inv, x[4 * i + 2] * inv, x[4 * i + 3] * inv);
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -15,16 +15,16 @@
 //
 // decode_kernel: one workgroup per (batch, head) unit.  K and V rows are
 //   streamed once with 16-byte non-temporal loads, a row spread over
-//   D*sizeof(T)/16 consecutive lanes (16 lanes for bf16 d = 128, 12 of a
-//   16-lane group for d = 96, 8 for d = 64).  Each row group keeps an online
-//   softmax (running max, running sum, running output), so K and V are read in
-//   the same pass; the groups are merged through LDS at the end.  Logits (log2
-//   domain) stay in LDS for the exact score update.  The argmin is a
-//   deterministic u64 minimum over (score bits << 32 | position): non-negative
-//   float bit patterns order like unsigned integers, so equal scores send the
-//   older position out.  The ring row that may move to the victim's slot and
-//   the new token's row are kept in LDS from the streaming pass, so admission
-//   writes at most two rows without reading them again.
+//   D*sizeof(C)/16 consecutive lanes (16 lanes for bf16 d = 128, 12 of a
+//   16-lane group for d = 96, 8 for d = 64; E4M3 rows take half as many).  Each
+//   row group keeps an online softmax (running max, running sum, running
+//   output), so K and V are read in the same pass; the groups are merged
+//   through LDS at the end.  Logits (log2 domain) stay in LDS for the exact
+//   score update.  The argmin is a deterministic u64 minimum over (score bits
+//   << 32 | position): non-negative float bit patterns order like unsigned
+//   integers, so equal scores send the older position out.  The ring row that
+//   may move to the victim's slot and the new token's row are kept in LDS from
+//   the streaming pass, so admission writes at most two rows.
 //
 // decode_split_kernel: for batches with few units, S workgroups share a unit,
 //   each streaming a contiguous range of its rows.  Every workgroup writes its
@@ -32,8 +32,15 @@
 //   unit's arrival counter; the last to arrive combines the partials, runs the
 //   score update and eviction, and resets the counter.  No workgroup waits for
 //   another.
+//
+// E4M3 cache (C = e4m3, bf16 inputs): slots hold E4M3 codes with one float32
+// scale per row; the K scale multiplies the row's logit and the V scale its
+// weight.  The decoded token attends with its exact bf16 row and is quantized
+// on admission: codes of x * (448 / amax), scale amax / 448.
 #include <float.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -53,18 +60,24 @@ __device__ inline unsigned long long shfl_xor_u64(unsigned long long x, int mask
   return ((unsigned long long)hi << 32) | lo;
 }
 
-template <typename T, int D, int NW>
+// T: input element type (q, k_new, v_new); C: cache element type.
+template <typename T, typename C, int D, int NW>
 struct Geo {
-  using E = Elem<T>;
-  static constexpr int EPL = E::kPer16B;     // elements per lane per row
+  using EC = Elem<C>;
+  using EI = Elem<T>;
+  static constexpr bool kQuant = std::is_same<C, e4m3>::value;
+  static constexpr int EPL = EC::kPer16B;    // elements per lane per row
   static constexpr int LPR = D / EPL;        // lanes holding one row
   static constexpr int G = ceil_pow2(LPR);   // lanes per row group
   static constexpr int RW = 64 / G;          // rows per wave per batch
   static constexpr int NG = NW * RW;         // row groups per workgroup
   static constexpr int NT = NW * 64;
-  static constexpr int ROWB = D * E::kBytes;
+  static constexpr int ROWB = D * EC::kBytes;   // cache row bytes
+  static constexpr int IROWB = D * EI::kBytes;  // input row bytes
+  static constexpr int ICH = EPL * EI::kBytes / 16;  // 16-byte input chunks per lane
   static constexpr int PF = 8;               // slots per thread prefetched for the score update
   static_assert(LPR * EPL == D && G <= 64, "row mapping");
+  static_assert(!kQuant || std::is_same<T, bf16>::value, "E4M3 cache takes bf16 inputs");
 };
 
 // One unit's step as seen by every thread.
@@ -81,7 +94,7 @@ struct StepView {
 };
 
 // Per-unit pointers.
-template <int ROWB>
+template <typename GG>
 struct UnitPtrs {
   char* K;
   char* V;
@@ -90,33 +103,49 @@ struct UnitPtrs {
   const char* q;
   float* score;
   int32_t* pos;
+  float* ks;
+  float* vs;
   __device__ UnitPtrs(const DecodeArgs& a, int unit, int k) {
     const size_t ubase = (size_t)unit * k;
-    K = (char*)a.k_slots + ubase * ROWB;
-    V = (char*)a.v_slots + ubase * ROWB;
-    kn = (const char*)a.k_new + (size_t)unit * ROWB;
-    vn = (const char*)a.v_new + (size_t)unit * ROWB;
-    q = (const char*)a.q + (size_t)unit * ROWB;
+    K = (char*)a.k_slots + ubase * GG::ROWB;
+    V = (char*)a.v_slots + ubase * GG::ROWB;
+    kn = (const char*)a.k_new + (size_t)unit * GG::IROWB;
+    vn = (const char*)a.v_new + (size_t)unit * GG::IROWB;
+    q = (const char*)a.q + (size_t)unit * GG::IROWB;
     score = a.score + ubase;
     pos = a.pos + ubase;
+    ks = GG::kQuant ? a.k_scale + ubase : nullptr;
+    vs = GG::kQuant ? a.v_scale + ubase : nullptr;
   }
 };
 
+// The EPL input-row elements lane chunk c covers, as floats.
+template <typename GG>
+__device__ inline void load_input(const char* row, int c, float* x) {
+#pragma unroll
+  for (int i = 0; i < GG::ICH; ++i)
+    GG::EI::unpack(load16(row + (c * GG::ICH + i) * 16), x + i * GG::EI::kPer16B);
+}
+
+// LDS stash of the rows the admission writes.
+template <typename GG>
+struct Stash {
+  uint4 ring[2][GG::LPR];  // K, V of the ring slot leaving the window
+  uint4 self[2][GG::LPR];  // K, V of the decoded token (cache format; not used for E4M3)
+  float ring_scale[2];     // E4M3 row scales of the ring row
+};
+
 // Streams logical rows [lo, hi): logit of each row into s_logit[j] (log2
-// domain), per-row-group online softmax into (m, lsum, o).  The new token's row
-// and the ring row leaving the window are copied into the LDS stash when they
-// fall in the range.  Loads are unconditional (rows outside the range and idle
-// lanes re-read a valid row and are masked out) so the compiler tracks
-// outstanding loads exactly; the next row batch is in flight while the current
-// one is consumed.
-template <typename T, int D, int NW>
-__device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<Geo<T, D, NW>::ROWB>& u,
-                                            int lo, int hi, const float* qf, float scale_log2,
-                                            float* s_logit, uint4 (*s_ring)[Geo<T, D, NW>::LPR],
-                                            uint4 (*s_self)[Geo<T, D, NW>::LPR], float& m,
-                                            float& lsum, float* o) {
-  using GG = Geo<T, D, NW>;
-  using E = typename GG::E;
+// domain), per-row-group online softmax into (m, lsum, o).  The rows the
+// admission writes are copied into the LDS stash when they fall in the range.
+// Loads are unconditional (rows outside the range and idle lanes re-read a
+// valid row and are masked out) so the compiler tracks outstanding loads
+// exactly; the next row batch is in flight while the current one is consumed.
+template <typename GG>
+__device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG>& u, int lo, int hi,
+                                            const float* qf, float scale_log2, float* s_logit,
+                                            Stash<GG>* st, float& m, float& lsum, float* o) {
+  using EC = typename GG::EC;
   constexpr int EPL = GG::EPL, G = GG::G, RW = GG::RW, NG = GG::NG, LPR = GG::LPR;
   const int lane = threadIdx.x & 63;
   const int gl = lane & (G - 1);
@@ -124,75 +153,150 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<Ge
   const bool act = gl < LPR;
   const int chunk = act ? gl : 0;
 
-  auto fetch = [&](int base, uint4& kr, uint4& vr) {
-    const int j = base + grp;
-    const char* kp = u.kn;
-    const char* vp = u.vn;
-    if (j < v.n_live && j < hi) {
-      const size_t off = (size_t)v.slot_of(j) * GG::ROWB;
-      kp = u.K + off;
-      vp = u.V + off;
-    }
-    kr = load16_stream(kp + chunk * 16);
-    vr = load16_stream(vp + chunk * 16);
-  };
-  auto consume = [&](int base, const uint4& kr, const uint4& vr) {
-    float kf[EPL];
-    E::unpack(kr, kf);
-    float d = 0.f;
+  if constexpr (!GG::kQuant) {
+    auto fetch = [&](int base, uint4& kr, uint4& vr) {
+      const int j = base + grp;
+      const char* kp = u.kn;
+      const char* vp = u.vn;
+      if (j < v.n_live && j < hi) {
+        const size_t off = (size_t)v.slot_of(j) * GG::ROWB;
+        kp = u.K + off;
+        vp = u.V + off;
+      }
+      kr = load16_stream(kp + chunk * 16);
+      vr = load16_stream(vp + chunk * 16);
+    };
+    auto consume = [&](int base, const uint4& kr, const uint4& vr) {
+      float kf[EPL];
+      EC::unpack(kr, kf);
+      float d = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) d = fmaf(qf[e], kf[e], d);  // qf is 0 on idle lanes
-    d = group_sum<G>(d);
-    const int j = base + grp;
-    const bool valid = j < hi;
-    const float lg = valid ? d * scale_log2 : -INFINITY;
-    if (valid) {
-      if (gl == 0) s_logit[j] = lg;
-      if (act) {
-        if (j == v.n_live) {
-          s_self[0][gl] = kr;
-          s_self[1][gl] = vr;
-        } else if (v.ring_live && j == v.ring_slot) {
-          s_ring[0][gl] = kr;
-          s_ring[1][gl] = vr;
+      for (int e = 0; e < EPL; ++e) d = fmaf(qf[e], kf[e], d);  // qf is 0 on idle lanes
+      d = group_sum<G>(d);
+      const int j = base + grp;
+      const bool valid = j < hi;
+      const float lg = valid ? d * scale_log2 : -INFINITY;
+      if (valid) {
+        if (gl == 0) s_logit[j] = lg;
+        if (act) {
+          if (j == v.n_live) {
+            st->self[0][gl] = kr;
+            st->self[1][gl] = vr;
+          } else if (v.ring_live && j == v.ring_slot) {
+            st->ring[0][gl] = kr;
+            st->ring[1][gl] = vr;
+          }
         }
       }
-    }
-    const float mn = fmaxf(m, lg);
-    if (mn > -INFINITY) {
-      const float alpha = fast_exp2(m - mn);
-      const float p = fast_exp2(lg - mn);  // 0 for rows outside the range
-      float vf[EPL];
-      E::unpack(vr, vf);
-      lsum = fmaf(lsum, alpha, p);
+      const float mn = fmaxf(m, lg);
+      if (mn > -INFINITY) {
+        const float alpha = fast_exp2(m - mn);
+        const float p = fast_exp2(lg - mn);  // 0 for rows outside the range
+        float vf[EPL];
+        EC::unpack(vr, vf);
+        lsum = fmaf(lsum, alpha, p);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vf[e], o[e] * alpha);
-      m = mn;
+        for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vf[e], o[e] * alpha);
+        m = mn;
+      }
+    };
+    uint4 ka, va, kb, vb;
+    fetch(lo, ka, va);
+    for (int base = lo; base < hi; base += 2 * NG) {
+      fetch(base + NG, kb, vb);
+      consume(base, ka, va);
+      fetch(base + 2 * NG, ka, va);
+      consume(base + NG, kb, vb);
     }
-  };
-
-  uint4 ka, va, kb, vb;
-  fetch(lo, ka, va);
-  for (int base = lo; base < hi; base += 2 * NG) {
-    fetch(base + NG, kb, vb);
-    consume(base, ka, va);
-    fetch(base + 2 * NG, ka, va);
-    consume(base + NG, kb, vb);
+  } else {
+    // The decoded token (exact bf16 row) seeds row group 0 when it is in range.
+    if (v.n_live >= lo && v.n_live < hi) {
+      float kx[EPL];
+      load_input<GG>(u.kn, chunk, kx);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) d = fmaf(qf[e], kx[e], d);
+      d = group_sum<G>(d);
+      const float ls = d * scale_log2;
+      if (grp == 0) {
+        if (gl == 0) s_logit[v.n_live] = ls;
+        float vx[EPL];
+        load_input<GG>(u.vn, chunk, vx);
+        m = ls;
+        lsum = 1.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] = act ? vx[e] : 0.f;
+      }
+    }
+    const int end = min(hi, v.n_live);  // cached rows only
+    auto fetch = [&](int base, uint4& kr, uint4& vr, float& ksc, float& vsc) {
+      const int j = base + grp;
+      const int s = (j < end) ? v.slot_of(j) : 0;  // slot 0 stands in past the end
+      const size_t off = (size_t)s * GG::ROWB;
+      kr = load16_stream(u.K + off + chunk * 16);
+      vr = load16_stream(u.V + off + chunk * 16);
+      ksc = u.ks[s];
+      vsc = u.vs[s];
+    };
+    auto consume = [&](int base, const uint4& kr, const uint4& vr, float ksc, float vsc) {
+      float kf[EPL];
+      EC::unpack(kr, kf);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) d = fmaf(qf[e], kf[e], d);
+      d = group_sum<G>(d);
+      const int j = base + grp;
+      const bool valid = j < end;
+      const float lg = valid ? d * ksc * scale_log2 : -INFINITY;
+      if (valid) {
+        if (gl == 0) s_logit[j] = lg;
+        if (v.ring_live && j == v.ring_slot) {
+          if (act) {
+            st->ring[0][gl] = kr;
+            st->ring[1][gl] = vr;
+          }
+          if (gl == 0) {
+            st->ring_scale[0] = ksc;
+            st->ring_scale[1] = vsc;
+          }
+        }
+      }
+      const float mn = fmaxf(m, lg);
+      if (mn > -INFINITY) {
+        const float alpha = fast_exp2(m - mn);
+        const float p = fast_exp2(lg - mn);
+        const float pv = p * vsc;
+        float vf[EPL];
+        EC::unpack(vr, vf);
+        lsum = fmaf(lsum, alpha, p);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] = fmaf(pv, vf[e], o[e] * alpha);
+        m = mn;
+      }
+    };
+    uint4 ka, va, kb, vb;
+    float ska, sva, skb, svb;
+    fetch(lo, ka, va, ska, sva);
+    for (int base = lo; base < end; base += 2 * NG) {
+      fetch(base + NG, kb, vb, skb, svb);
+      consume(base, ka, va, ska, sva);
+      fetch(base + 2 * NG, ka, va, ska, sva);
+      consume(base + NG, kb, vb, skb, svb);
+    }
   }
 }
 
 // Workgroup merge of the row groups: leaves M (block max), the group weights
 // and L (block sum) in registers of every thread; s_o keeps the group outputs.
-template <int NG, int D>
+template <int NG>
 struct GroupMerge {
   float M, L;
   float wg[NG];
 };
 
-template <typename T, int D, int NW>
-__device__ __forceinline__ GroupMerge<Geo<T, D, NW>::NG, D> merge_groups(
-    float m, float lsum, const float* o, float (*s_o)[D], float* s_m, float* s_l) {
-  using GG = Geo<T, D, NW>;
+template <typename GG, int D>
+__device__ __forceinline__ GroupMerge<GG::NG> merge_groups(float m, float lsum, const float* o,
+                                                           float (*s_o)[D], float* s_m, float* s_l) {
   constexpr int EPL = GG::EPL, G = GG::G, RW = GG::RW, NG = GG::NG, LPR = GG::LPR;
   const int lane = threadIdx.x & 63;
   const int gl = lane & (G - 1);
@@ -206,7 +310,7 @@ __device__ __forceinline__ GroupMerge<Geo<T, D, NW>::NG, D> merge_groups(
     for (int e = 0; e < EPL; ++e) s_o[grp][gl * EPL + e] = o[e];
   }
   __syncthreads();
-  GroupMerge<NG, D> r;
+  GroupMerge<NG> r;
   r.M = -INFINITY;
 #pragma unroll
   for (int g = 0; g < NG; ++g) r.M = fmaxf(r.M, s_m[g]);
@@ -220,19 +324,39 @@ __device__ __forceinline__ GroupMerge<Geo<T, D, NW>::NG, D> merge_groups(
   return r;
 }
 
+// Quantize the decoded token's K and V rows into the ring slot (E4M3 cache):
+// lanes [0, G) of wave 0 take K, lanes [G, 2G) take V, each lane 16 values.
+template <typename GG>
+__device__ inline void admit_quantized(const StepView& v, const UnitPtrs<GG>& u) {
+  constexpr int G = GG::G, LPR = GG::LPR, EPL = GG::EPL;
+  const int tid = threadIdx.x;
+  if (tid >= 2 * G) return;
+  const bool is_v = tid >= G;
+  const int c = tid & (G - 1);
+  const bool act = c < LPR;
+  float x[EPL];
+  load_input<GG>(is_v ? u.vn : u.kn, act ? c : 0, x);
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  amax = group_max<G>(act ? amax : 0.f);
+  char* row = (is_v ? u.V : u.K) + (size_t)v.ring_slot * GG::ROWB;
+  if (act) store16(row + c * 16, quantize16_e4m3(x, amax));
+  if (c == 0) (is_v ? u.vs : u.ks)[v.ring_slot] = __fdiv_rn(amax, 448.f);
+}
+
 // Score update, eviction argmin and admission for one unit, given the exact
 // softmax max M and 1/L.  Logits of rows [0, n_att) are in s_logit; the
 // scores this thread owns were prefetched into sc_pf / ps_pf; the ring row and
-// the new token's row are in the LDS stash.
-template <typename T, int D, int NW>
-__device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<Geo<T, D, NW>::ROWB>& u,
-                                            float M, float invL, float* s_logit, const float* sc_pf,
-                                            const int* ps_pf, uint4 (*s_ring)[Geo<T, D, NW>::LPR],
-                                            uint4 (*s_self)[Geo<T, D, NW>::LPR],
+// (unquantized caches) the new token's row are in the LDS stash.
+template <typename GG>
+__device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG>& u, float M,
+                                            float invL, float* s_logit, const float* sc_pf,
+                                            const int* ps_pf, const Stash<GG>* st,
                                             unsigned long long* s_key, int* s_victim,
                                             int32_t* evicted, int unit) {
-  using GG = Geo<T, D, NW>;
   constexpr int NT = GG::NT, PF = GG::PF, LPR = GG::LPR, ROWB = GG::ROWB;
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -303,26 +427,31 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<Ge
     if (dst >= 0) {
       u.score[dst] = s_logit[v.ring_slot];
       u.pos[dst] = v.t - v.r;
+      if constexpr (GG::kQuant) {
+        u.ks[dst] = st->ring_scale[0];
+        u.vs[dst] = st->ring_scale[1];
+      }
     }
     u.score[v.ring_slot] = p_self;
     u.pos[v.ring_slot] = v.t;
     if (evicted) evicted[unit] = v.full ? (int32_t)(uint32_t)vkey : -1;
   }
-  if (tid < LPR) {
-    if (dst >= 0) {
-      store16(u.K + (size_t)dst * ROWB + tid * 16, s_ring[0][tid]);
-      store16(u.V + (size_t)dst * ROWB + tid * 16, s_ring[1][tid]);
-    }
-    store16(u.K + (size_t)v.ring_slot * ROWB + tid * 16, s_self[0][tid]);
-    store16(u.V + (size_t)v.ring_slot * ROWB + tid * 16, s_self[1][tid]);
+  if (tid < LPR && dst >= 0) {
+    store16(u.K + (size_t)dst * ROWB + tid * 16, st->ring[0][tid]);
+    store16(u.V + (size_t)dst * ROWB + tid * 16, st->ring[1][tid]);
+  }
+  if constexpr (GG::kQuant) {
+    admit_quantized<GG>(v, u);
+  } else if (tid < LPR) {
+    store16(u.K + (size_t)v.ring_slot * ROWB + tid * 16, st->self[0][tid]);
+    store16(u.V + (size_t)v.ring_slot * ROWB + tid * 16, st->self[1][tid]);
   }
 }
 
 // Prefetch of the scores a thread will update, and of the candidates' positions.
-template <typename T, int D, int NW>
-__device__ __forceinline__ void prefetch_scores(const StepView& v, const UnitPtrs<Geo<T, D, NW>::ROWB>& u,
-                                                float* sc_pf, int* ps_pf) {
-  using GG = Geo<T, D, NW>;
+template <typename GG>
+__device__ __forceinline__ void prefetch_scores(const StepView& v, const UnitPtrs<GG>& u, float* sc_pf,
+                                                int* ps_pf) {
 #pragma unroll
   for (int i = 0; i < GG::PF; ++i) {
     const int j = threadIdx.x + i * GG::NT;
@@ -336,17 +465,15 @@ __device__ __forceinline__ void prefetch_scores(const StepView& v, const UnitPtr
   }
 }
 
-template <typename T, int D, int NW>
+template <typename T, typename C, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
-  using GG = Geo<T, D, NW>;
-  using E = typename GG::E;
+  using GG = Geo<T, C, D, NW>;
   constexpr int EPL = GG::EPL, LPR = GG::LPR, NG = GG::NG, NT = GG::NT, PF = GG::PF;
 
   __shared__ float s_o[NG][D];
   __shared__ float s_m[NG];
   __shared__ float s_l[NG];
-  __shared__ uint4 s_ring[2][LPR];  // K, V of the ring slot leaving the window
-  __shared__ uint4 s_self[2][LPR];  // K, V of the decoded token
+  __shared__ Stash<GG> st;
   __shared__ unsigned long long s_key[NW];
   __shared__ int s_victim;
   extern __shared__ float s_logit[];  // [n_live + 1] logits, later updated scores
@@ -354,25 +481,29 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int unit = blockIdx.x;
   const int tid = threadIdx.x;
   const StepView v(a);
-  const UnitPtrs<GG::ROWB> u(a, unit, v.k);
+  const UnitPtrs<GG> u(a, unit, v.k);
   const int gl = (tid & 63) & (GG::G - 1);
   const bool act = gl < LPR;
 
   if (tid == 0) s_victim = v.ring_slot;  // overwritten by the argmin owner when the cache is full
 
   float qf[EPL];
-  E::unpack(act ? load16(u.q + gl * 16) : make_uint4(0, 0, 0, 0), qf);
+  load_input<GG>(u.q, act ? gl : 0, qf);
+  if (!act) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[e] = 0.f;
+  }
   float sc_pf[PF];
   int ps_pf[PF];
-  prefetch_scores<T, D, NW>(v, u, sc_pf, ps_pf);
+  prefetch_scores<GG>(v, u, sc_pf, ps_pf);
 
   float m = -INFINITY, lsum = 0.f;
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  stream_rows<T, D, NW>(v, u, 0, v.n_att, qf, a.scale_log2, s_logit, s_ring, s_self, m, lsum, o);
+  stream_rows<GG>(v, u, 0, v.n_att, qf, a.scale_log2, s_logit, &st, m, lsum, o);
 
-  const GroupMerge<NG, D> gm = merge_groups<T, D, NW>(m, lsum, o, s_o, s_m, s_l);
+  const GroupMerge<NG> gm = merge_groups<GG, D>(m, lsum, o, s_o, s_m, s_l);
   const float invL = 1.f / gm.L;
   for (int c = tid; c < D; c += NT) {
     float acc = 0.f;
@@ -380,22 +511,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     for (int g = 0; g < NG; ++g) acc = fmaf(s_o[g][c], gm.wg[g], acc);
     a.out[(size_t)unit * D + c] = acc * invL;
   }
-  finish_step<T, D, NW>(v, u, gm.M, invL, s_logit, sc_pf, ps_pf, s_ring, s_self, s_key, &s_victim,
-                        a.evicted, unit);
+  finish_step<GG>(v, u, gm.M, invL, s_logit, sc_pf, ps_pf, &st, s_key, &s_victim, a.evicted, unit);
 }
 
-template <typename T, int D, int NW>
+template <typename T, typename C, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, SplitScratch sp) {
-  using GG = Geo<T, D, NW>;
-  using E = typename GG::E;
+  using GG = Geo<T, C, D, NW>;
   constexpr int EPL = GG::EPL, LPR = GG::LPR, NG = GG::NG, NT = GG::NT, PF = GG::PF;
   constexpr int ROWB = GG::ROWB;
 
   __shared__ float s_o[NG][D];
   __shared__ float s_m[NG];
   __shared__ float s_l[NG];
-  __shared__ uint4 s_ring[2][LPR];
-  __shared__ uint4 s_self[2][LPR];
+  __shared__ Stash<GG> st;
   __shared__ unsigned long long s_key[NW];
   __shared__ int s_victim;
   __shared__ int s_last;
@@ -406,17 +534,21 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   const int part = blockIdx.x % S;
   const int tid = threadIdx.x;
   const StepView v(a);
-  const UnitPtrs<ROWB> u(a, unit, v.k);
+  const UnitPtrs<GG> u(a, unit, v.k);
   const int gl = (tid & 63) & (GG::G - 1);
   const bool act = gl < LPR;
 
   if (tid == 0) s_victim = v.ring_slot;
 
   float qf[EPL];
-  E::unpack(act ? load16(u.q + gl * 16) : make_uint4(0, 0, 0, 0), qf);
+  load_input<GG>(u.q, act ? gl : 0, qf);
+  if (!act) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[e] = 0.f;
+  }
   float sc_pf[PF];
   int ps_pf[PF];
-  prefetch_scores<T, D, NW>(v, u, sc_pf, ps_pf);
+  prefetch_scores<GG>(v, u, sc_pf, ps_pf);
 
   const int per = (v.n_att + S - 1) / S;
   const int lo = min(v.n_att, part * per);
@@ -425,8 +557,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  stream_rows<T, D, NW>(v, u, lo, hi, qf, a.scale_log2, s_logit, s_ring, s_self, m, lsum, o);
-  const GroupMerge<NG, D> gm = merge_groups<T, D, NW>(m, lsum, o, s_o, s_m, s_l);
+  stream_rows<GG>(v, u, lo, hi, qf, a.scale_log2, s_logit, &st, m, lsum, o);
+  const GroupMerge<NG> gm = merge_groups<GG, D>(m, lsum, o, s_o, s_m, s_l);
 
   // This workgroup's partial: max, sum, output relative to its max; its logits.
   float* pp = sp.partials + ((size_t)unit * S + part) * (D + 2);
@@ -477,54 +609,61 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
     }
     a.out[(size_t)unit * D + d] = acc * invL;
   }
-  // All logits, and the two rows the admission writes (still intact: only this
+  // All logits, and the rows the admission writes (still intact: only this
   // workgroup writes the unit's state).
   for (int j = tid; j < v.n_att; j += NT) s_logit[j] = lg[j];
   if (tid < LPR) {
-    s_self[0][tid] = load16(u.kn + tid * 16);
-    s_self[1][tid] = load16(u.vn + tid * 16);
+    if constexpr (!GG::kQuant) {
+      st.self[0][tid] = load16(u.kn + tid * 16);
+      st.self[1][tid] = load16(u.vn + tid * 16);
+    }
     if (v.ring_live) {
-      s_ring[0][tid] = load16(u.K + (size_t)v.ring_slot * ROWB + tid * 16);
-      s_ring[1][tid] = load16(u.V + (size_t)v.ring_slot * ROWB + tid * 16);
+      st.ring[0][tid] = load16(u.K + (size_t)v.ring_slot * ROWB + tid * 16);
+      st.ring[1][tid] = load16(u.V + (size_t)v.ring_slot * ROWB + tid * 16);
+    }
+  }
+  if constexpr (GG::kQuant) {
+    if (tid == 0 && v.ring_live) {
+      st.ring_scale[0] = u.ks[v.ring_slot];
+      st.ring_scale[1] = u.vs[v.ring_slot];
     }
   }
   __syncthreads();
-  finish_step<T, D, NW>(v, u, M, invL, s_logit, sc_pf, ps_pf, s_ring, s_self, s_key, &s_victim,
-                        a.evicted, unit);
+  finish_step<GG>(v, u, M, invL, s_logit, sc_pf, ps_pf, &st, s_key, &s_victim, a.evicted, unit);
   if (tid == 0) sp.counters[unit] = 0u;  // ready for the next step
 }
 
-template <typename T, int D, int NW>
+template <typename T, typename C, int D, int NW>
 hipError_t launch_nw(const DecodeArgs& a, const SplitScratch* sp, hipStream_t s) {
   const int n_live = a.n_ring + a.n_heavy;
   const size_t lds = (size_t)(n_live + 1) * sizeof(float);
   if (sp && sp->splits > 1) {
-    hipLaunchKernelGGL((decode_split_kernel<T, D, NW>), dim3(a.units * sp->splits), dim3(NW * 64),
-                       lds, s, a, *sp);
+    hipLaunchKernelGGL((decode_split_kernel<T, C, D, NW>), dim3(a.units * sp->splits),
+                       dim3(NW * 64), lds, s, a, *sp);
   } else {
-    hipLaunchKernelGGL((decode_kernel<T, D, NW>), dim3(a.units), dim3(NW * 64), lds, s, a);
+    hipLaunchKernelGGL((decode_kernel<T, C, D, NW>), dim3(a.units), dim3(NW * 64), lds, s, a);
   }
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, typename C, int D>
 hipError_t launch_d(const DecodeArgs& a, int waves, const SplitScratch* sp, hipStream_t s) {
   switch (waves) {
-    case 1: return launch_nw<T, D, 1>(a, sp, s);
-    case 2: return launch_nw<T, D, 2>(a, sp, s);
-    case 4: return launch_nw<T, D, 4>(a, sp, s);
-    case 8: return launch_nw<T, D, 8>(a, sp, s);
+    case 1: return launch_nw<T, C, D, 1>(a, sp, s);
+    case 2: return launch_nw<T, C, D, 2>(a, sp, s);
+    case 4: return launch_nw<T, C, D, 4>(a, sp, s);
+    case 8: return launch_nw<T, C, D, 8>(a, sp, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T>
+template <typename T, typename C>
 hipError_t launch_t(const DecodeArgs& a, int head_dim, int waves, const SplitScratch* sp,
                     hipStream_t s) {
   switch (head_dim) {
-    case 64: return launch_d<T, 64>(a, waves, sp, s);
-    case 96: return launch_d<T, 96>(a, waves, sp, s);
-    case 128: return launch_d<T, 128>(a, waves, sp, s);
+    case 64: return launch_d<T, C, 64>(a, waves, sp, s);
+    case 96: return launch_d<T, C, 96>(a, waves, sp, s);
+    case 128: return launch_d<T, C, 128>(a, waves, sp, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -539,15 +678,22 @@ int decode_waves_auto(int units) {
 }
 
 int decode_split_auto(int units, int waves) {
-  (void)waves;
+  // Measured on MI355X: the agent-scope publication of the partials costs more
+  // than the split gains at every small workload tried, so one workgroup per
+  // unit is the default.
   (void)units;
+  (void)waves;
   return 1;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int waves,
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int cache, int head_dim, int waves,
                          const SplitScratch* sp, hipStream_t s) {
-  if (dtype == 0) return launch_t<float>(a, head_dim, waves, sp, s);
-  if (dtype == 1) return launch_t<bf16>(a, head_dim, waves, sp, s);
+  if (cache == 1) {
+    if (dtype != 1) return hipErrorInvalidValue;
+    return launch_t<bf16, e4m3>(a, head_dim, waves, sp, s);
+  }
+  if (dtype == 0) return launch_t<float, float>(a, head_dim, waves, sp, s);
+  if (dtype == 1) return launch_t<bf16, bf16>(a, head_dim, waves, sp, s);
   return hipErrorInvalidValue;
 }
 

@@ -37,7 +37,9 @@ bool valid_dims(const h2o_config* c) {
          isfinite(c->scale) && c->scale >= 0.f && c->start_pos >= 0 && c->start_live >= 0 &&
          (c->decode_waves == 0 || c->decode_waves == 1 || c->decode_waves == 2 ||
           c->decode_waves == 4 || c->decode_waves == 8) &&
-         c->decode_split >= 0 && c->decode_split <= 64;
+         c->decode_split >= 0 && c->decode_split <= 64 &&
+         (c->cache_dtype == H2O_CACHE_INPUT ||
+          (c->cache_dtype == H2O_CACHE_E4M3 && c->kv_dtype == H2O_BF16));
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -59,6 +61,9 @@ h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** o
       !aligned16(state->pos))
     return H2O_ERR_INVALID;
   if (!valid_dims(cfg)) return H2O_ERR_INVALID;
+  if (cfg->cache_dtype == H2O_CACHE_E4M3 &&
+      (!state->k_scale || !state->v_scale || !aligned16(state->k_scale) || !aligned16(state->v_scale)))
+    return H2O_ERR_INVALID;
   if (cfg->head_dim != 64 && cfg->head_dim != 96 && cfg->head_dim != 128) return H2O_ERR_UNSUPPORTED;
   const int64_t k = (int64_t)cfg->recent + cfg->heavy;
   if (k > H2O_MAX_K) return H2O_ERR_UNSUPPORTED;
@@ -135,6 +140,8 @@ h2o_status h2o_prefill(h2o_ctx* ctx, const void* q, const void* k, const void* v
   a.v_slots = ctx->st.v_slots;
   a.score = ctx->st.score;
   a.pos = ctx->st.pos;
+  a.k_scale = ctx->st.k_scale;
+  a.v_scale = ctx->st.v_scale;
   a.row_lse = ctx->scratch;
   a.colsum = ctx->scratch + units * ctx->stride;
   a.units = (int32_t)units;
@@ -144,8 +151,8 @@ h2o_status h2o_prefill(h2o_ctx* ctx, const void* q, const void* k, const void* v
   a.r = ctx->cfg.recent;
   a.h = ctx->cfg.heavy;
   a.scale_log2 = ctx->scale_log2;
-  const hipError_t e = h2o::launch_prefill(a, ctx->cfg.kv_dtype, ctx->cfg.head_dim,
-                                           (hipStream_t)stream);
+  const hipError_t e = h2o::launch_prefill(a, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype,
+                                           ctx->cfg.head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return from_hip(e);
   ctx->t = prompt_len;
   ctx->n_live = prompt_len < ctx->k ? prompt_len : ctx->k;
@@ -170,6 +177,8 @@ h2o_status enqueue_step(h2o_ctx* ctx, const void* q, const void* k_new, const vo
   a.v_slots = ctx->st.v_slots;
   a.score = ctx->st.score;
   a.pos = ctx->st.pos;
+  a.k_scale = ctx->st.k_scale;
+  a.v_scale = ctx->st.v_scale;
   a.out = out;
   a.evicted = evicted_pos;
   a.units = ctx->cfg.batch * ctx->cfg.heads;
@@ -179,8 +188,8 @@ h2o_status enqueue_step(h2o_ctx* ctx, const void* q, const void* k_new, const vo
   a.n_ring = n_ring;
   a.n_heavy = ctx->n_live - n_ring;
   a.scale_log2 = ctx->scale_log2;
-  const hipError_t e = h2o::launch_decode(a, ctx->cfg.kv_dtype, ctx->cfg.head_dim, ctx->waves,
-                                          &ctx->split, stream);
+  const hipError_t e = h2o::launch_decode(a, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype,
+                                          ctx->cfg.head_dim, ctx->waves, &ctx->split, stream);
   if (e != hipSuccess) return from_hip(e);
   ctx->t += 1;
   if (ctx->n_live < ctx->k) ctx->n_live += 1;

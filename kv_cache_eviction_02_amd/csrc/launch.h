@@ -14,6 +14,8 @@ struct DecodeArgs {
   void* v_slots;       // [U, k, d]
   float* score;        // [U, k]
   int32_t* pos;        // [U, k]
+  float* k_scale;      // [U, k] E4M3 row scales (E4M3 cache only)
+  float* v_scale;      // [U, k]
   float* out;          // [U, d]
   int32_t* evicted;    // [U] or null
   int32_t units;
@@ -40,6 +42,8 @@ struct PrefillArgs {
   void* v_slots;
   float* score;
   int32_t* pos;
+  float* k_scale;      // E4M3 cache only
+  float* v_scale;
   float* row_lse;      // scratch [U, stride]: per query row, log2 of the softmax denominator (log2 domain)
   float* colsum;       // scratch [U, stride]: accumulated attention per prompt position
   int32_t units;
@@ -49,11 +53,13 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-// dtype: 0 = float32, 1 = bfloat16.  Return hipSuccess or the launch error.
+// dtype: 0 = float32, 1 = bfloat16 (inputs); cache: 0 = slots in the input
+// dtype, 1 = E4M3 codes with per-row scales (bf16 inputs only).  Return
+// hipSuccess or the launch error.
 // sp == nullptr or sp->splits < 2: one workgroup per unit.
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int waves,
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int cache, int head_dim, int waves,
                          const SplitScratch* sp, hipStream_t s);
-hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int cache, int head_dim, hipStream_t s);
 
 // Automatic wavefronts per unit for the decode kernel.
 int decode_waves_auto(int units);

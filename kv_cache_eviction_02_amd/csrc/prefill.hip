@@ -18,7 +18,8 @@
 //              tiles in a fixed order, so the sums are deterministic without
 //              atomics;
 //   select   : per unit, radix select of the h largest c_j among the older
-//              positions, then the gather of the kept K/V rows into slots.
+//              positions, then the gather of the kept K/V rows into slots
+//              (quantized to E4M3 with per-row scales for an E4M3 cache).
 //
 // MFMA use: v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (f32).
 // Lane l supplies row l % 16 of a 16-row tile and the contiguous quarter
@@ -27,6 +28,8 @@
 // 16x16 result lands as acc[i] = dot(moving row 4 * (l / 16) + i, fixed row l % 16).
 #include <float.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -292,10 +295,57 @@ __device__ inline int block_exclusive_scan(int v, int* buf, int* total) {
   return incl - v;
 }
 
-template <typename T, int D>
+constexpr int ceil_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Cooperative copy of prompt rows into cache slots.  Unquantized caches move
+// 16-byte chunks; an E4M3 cache gives each row an aligned group of lanes,
+// 16 values per lane, which agree on the row maximum and write the codes of
+// x * (448 / amax) and the row scale amax / 448.
+template <typename T, typename C, int D>
+struct RowCopy {
+  static constexpr bool kQuant = std::is_same<C, e4m3>::value;
+  static constexpr int IROWB = D * Elem<T>::kBytes;   // prompt row bytes
+  static constexpr int CROWB = D * Elem<C>::kBytes;   // slot row bytes
+  static constexpr int ITEMS = kQuant ? D / 16 : IROWB / 16;  // work items per row
+  static constexpr int GW = kQuant ? ceil_pow2(ITEMS) : ITEMS;  // loop slots per row
+
+  // item c (0 <= c < GW) of prompt row p -> slot sl
+  __device__ static inline void item(const PrefillArgs& a, int unit, int P, int k, int p, int sl, int c) {
+    const char* Kp = (const char*)a.pk + ((size_t)unit * P + p) * IROWB;
+    const char* Vp = (const char*)a.pv + ((size_t)unit * P + p) * IROWB;
+    char* Ks = (char*)a.k_slots + ((size_t)unit * k + sl) * CROWB;
+    char* Vs = (char*)a.v_slots + ((size_t)unit * k + sl) * CROWB;
+    if constexpr (!kQuant) {
+      store16(Ks + c * 16, load16(Kp + c * 16));
+      store16(Vs + c * 16, load16(Vp + c * 16));
+    } else {
+      const bool act = c < ITEMS;
+      const int cc = act ? c : 0;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const char* src = w ? Vp : Kp;
+        float x[16];
+        Elem<T>::unpack(load16(src + cc * 32), x);
+        Elem<T>::unpack(load16(src + cc * 32 + 16), x + 8);
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+        amax = group_max<GW>(act ? amax : 0.f);
+        if (act) store16((w ? Vs : Ks) + c * 16, quantize16_e4m3(x, amax));
+        if (c == 0) (w ? a.v_scale : a.k_scale)[(size_t)unit * k + sl] = __fdiv_rn(amax, 448.f);
+      }
+    }
+  }
+};
+
+template <typename T, typename C, int D>
 __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs a, int stride) {
-  constexpr int ROWB = D * Elem<T>::kBytes;
-  constexpr int CH = ROWB / 16;  // 16-byte chunks per row
+  using RC = RowCopy<T, C, D>;
+  constexpr int GW = RC::GW;
   __shared__ int hist[256];
   __shared__ int buf[kSelThreads];
   __shared__ int s_slot[kSelThreads];
@@ -310,10 +360,6 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs 
   const bool keep_all = n_pool <= h;
   const int n_sel = keep_all ? n_pool : h;
 
-  const char* Kp = (const char*)a.pk + (size_t)unit * P * ROWB;
-  const char* Vp = (const char*)a.pv + (size_t)unit * P * ROWB;
-  char* Ks = (char*)a.k_slots + (size_t)unit * k * ROWB;
-  char* Vs = (char*)a.v_slots + (size_t)unit * k * ROWB;
   float* score = a.score + (size_t)unit * k;
   int32_t* pos = a.pos + (size_t)unit * k;
 
@@ -378,14 +424,11 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs 
       pos[slot] = p;
     }
     __syncthreads();
-    for (int idx = tid; idx < kSelThreads * CH; idx += kSelThreads) {
-      const int x = idx / CH, part = idx % CH;
+    // GW consecutive lanes per row: whole groups are in or out of the loop together
+    for (int idx = tid; idx < kSelThreads * GW; idx += kSelThreads) {
+      const int x = idx / GW;
       const int sl = s_slot[x];
-      if (sl >= 0) {
-        const int pp = hi - 1 - x;
-        store16(Ks + (size_t)sl * ROWB + part * 16, load16(Kp + (size_t)pp * ROWB + part * 16));
-        store16(Vs + (size_t)sl * ROWB + part * 16, load16(Vp + (size_t)pp * ROWB + part * 16));
-      }
+      if (sl >= 0) RC::item(a, unit, P, k, hi - 1 - x, sl, idx % GW);
     }
     __syncthreads();
   }
@@ -396,10 +439,9 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs 
     score[p % r] = c[p];
     pos[p % r] = p;
   }
-  for (int idx = tid; idx < n_ring * CH; idx += kSelThreads) {
-    const int p = P - n_ring + idx / CH, part = idx % CH;
-    store16(Ks + (size_t)(p % r) * ROWB + part * 16, load16(Kp + (size_t)p * ROWB + part * 16));
-    store16(Vs + (size_t)(p % r) * ROWB + part * 16, load16(Vp + (size_t)p * ROWB + part * 16));
+  for (int idx = tid; idx < n_ring * GW; idx += kSelThreads) {
+    const int p = P - n_ring + idx / GW;
+    RC::item(a, unit, P, k, p, p % r, idx % GW);
   }
   // Unused slots.
   for (int s = tid; s < k; s += kSelThreads) {
@@ -411,7 +453,7 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs 
   }
 }
 
-template <typename T, int D>
+template <typename T, typename C, int D>
 hipError_t launch_prefill_td(const PrefillArgs& a, int stride, hipStream_t s) {
   constexpr int rows_per_block = kWaves * rows_per_wave<T>();
   const int nblk = (a.P + rows_per_block - 1) / rows_per_block;
@@ -422,26 +464,31 @@ hipError_t launch_prefill_td(const PrefillArgs& a, int stride, hipStream_t s) {
   hipLaunchKernelGGL((colsum_kernel<T, D>), grid, dim3(kWaves * 64), 0, s, a, stride, nblk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((select_gather_kernel<T, D>), dim3(a.units), dim3(kSelThreads), 0, s, a, stride);
+  hipLaunchKernelGGL((select_gather_kernel<T, C, D>), dim3(a.units), dim3(kSelThreads), 0, s, a,
+                     stride);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, typename C>
 hipError_t launch_prefill_t(const PrefillArgs& a, int head_dim, int stride, hipStream_t s) {
   switch (head_dim) {
-    case 64: return launch_prefill_td<T, 64>(a, stride, s);
-    case 96: return launch_prefill_td<T, 96>(a, stride, s);
-    case 128: return launch_prefill_td<T, 128>(a, stride, s);
+    case 64: return launch_prefill_td<T, C, 64>(a, stride, s);
+    case 96: return launch_prefill_td<T, C, 96>(a, stride, s);
+    case 128: return launch_prefill_td<T, C, 128>(a, stride, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, hipStream_t s) {
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int cache, int head_dim, hipStream_t s) {
   const int stride = a.stride;
-  if (dtype == 0) return launch_prefill_t<float>(a, head_dim, stride, s);
-  if (dtype == 1) return launch_prefill_t<bf16>(a, head_dim, stride, s);
+  if (cache == 1) {
+    if (dtype != 1) return hipErrorInvalidValue;
+    return launch_prefill_t<bf16, e4m3>(a, head_dim, stride, s);
+  }
+  if (dtype == 0) return launch_prefill_t<float, float>(a, head_dim, stride, s);
+  if (dtype == 1) return launch_prefill_t<bf16, bf16>(a, head_dim, stride, s);
   return hipErrorInvalidValue;
 }
 

@@ -23,7 +23,8 @@ import math
 import numpy as np
 import torch
 
-from oracle import decode_step, members_from_slots, prefill
+from oracle import (decode_step, dequantize_row_e4m3, members_from_slots, prefill,
+                    quantize_row_e4m3)
 from synth import gen
 from synth.stage import stage_decode, stage_prompt
 
@@ -68,27 +69,43 @@ def torch_dtype(wl):
 class Harness:
     """Runs one workload on the GPU and checks sampled units against the oracle."""
 
-    def __init__(self, wl, units, steps, device="cuda", decode_waves=0, decode_split=0):
+    def __init__(self, wl, units, steps, device="cuda", decode_waves=0, decode_split=0,
+                 cache="input"):
         self.wl = wl
         self.units = units
         self.steps = steps
         self.device = device
         self.stats = Stats()
+        self.cache_kind = cache
         U, k = wl.units, wl.k
         self.idx = torch.tensor(units, dtype=torch.long, device=device)
         self.cache = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy,
                               max_prompt=wl.prompt, dtype=torch_dtype(wl), scale=wl.scale,
-                              device=device, decode_waves=decode_waves, decode_split=decode_split)
+                              device=device, decode_waves=decode_waves, decode_split=decode_split,
+                              cache=cache)
         self.flat = dict(pos=self.cache.pos.view(U, k), score=self.cache.score.view(U, k),
                          k=self.cache.k_slots.view(U, k, -1), v=self.cache.v_slots.view(U, k, -1))
+        if cache == "e4m3":
+            self.flat["ks"] = self.cache.k_scale.view(U, k)
+            self.flat["vs"] = self.cache.v_scale.view(U, k)
         # exact input values and storage bits of the sampled units, all positions used
         n_pos = wl.prompt + steps
         self.vals = {}
         self.bits = {}
+        self.quant = {}
+        self.cached = {}
         for u in units:
             b, h = divmod(u, wl.heads)
             self.vals[u] = gen.unit_values(wl, b, h, 0, n_pos)
             self.bits[u] = gen.unit_storage(wl, b, h, 0, n_pos)
+            if cache == "e4m3":
+                # every cached row is the E4M3 form of its input row
+                qk = [quantize_row_e4m3(row) for row in self.vals[u][1]]
+                qv = [quantize_row_e4m3(row) for row in self.vals[u][2]]
+                self.quant[u] = (np.array([c for c, _ in qk]), np.array([s for _, s in qk], np.float32),
+                                 np.array([c for c, _ in qv]), np.array([s for _, s in qv], np.float32))
+                self.cached[u] = (np.array([dequantize_row_e4m3(c, s) for c, s in qk]),
+                                  np.array([dequantize_row_e4m3(c, s) for c, s in qv]))
 
     def gather(self, name):
         return self.flat[name].index_select(0, self.idx).cpu().numpy()
@@ -136,6 +153,18 @@ class Harness:
         pos = self.gather("pos")
         ks = self.flat["k"].index_select(0, self.idx).cpu()
         vs = self.flat["v"].index_select(0, self.idx).cpu()
+        if self.cache_kind == "e4m3":
+            ksc, vsc = self.gather("ks"), self.gather("vs")
+            ks, vs = ks.numpy(), vs.numpy()
+            for i, u in enumerate(self.units):
+                qkc, qks, qvc, qvs = self.quant[u]
+                live = np.flatnonzero(pos[i] >= 0)
+                p = pos[i][live]
+                np.testing.assert_array_equal(ks[i][live], qkc[p])
+                np.testing.assert_array_equal(vs[i][live], qvc[p])
+                np.testing.assert_array_equal(ksc[i][live], qks[p])
+                np.testing.assert_array_equal(vsc[i][live], qvs[p])
+            return
         if self.wl.kv_dtype == "bf16":
             ks = ks.view(torch.int16).numpy().view(np.uint16)
             vs = vs.view(torch.int16).numpy().view(np.uint16)
@@ -177,7 +206,8 @@ class Harness:
         for i, u in enumerate(self.units):
             Q, K, V = self.vals[u]
             members = members_from_slots(before[0][i], before[1][i])
-            res = decode_step(members, t, Q[t], K, V, r, h, wl.scale)
+            Kc, Vc = self.cached.get(u, (None, None))
+            res = decode_step(members, t, Q[t], K, V, r, h, wl.scale, Kc, Vc)
             scale_o = np.abs(res.out).max()
             err_o = np.abs(out[i] - res.out).max()
             assert err_o <= 2e-3 * scale_o, (u, t, err_o, scale_o)

@@ -25,13 +25,13 @@ def header_functions():
 def cfg(**kw):
     base = dict(batch=2, heads=3, head_dim=64, recent=4, heavy=4, max_prompt=0,
                 kv_dtype=B.H2O_BF16, scale=0.0, start_pos=0, start_live=0, decode_waves=0,
-                decode_split=0)
+                decode_split=0, cache_dtype=0)
     base.update(kw)
     return B.h2o_config(**base)
 
 
-def state(k=FAKE, v=FAKE, s=FAKE, p=FAKE):
-    return B.h2o_state(k, v, s, p)
+def state(k=FAKE, v=FAKE, s=FAKE, p=FAKE, ks=None, vs=None):
+    return B.h2o_state(k, v, s, p, ks, vs)
 
 
 def test_library_exports_every_header_function():
@@ -54,9 +54,10 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stdio.h>
 #include "h2o.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(h2o_config), offsetof(h2o_config, scale),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(h2o_config), offsetof(h2o_config, scale),
          offsetof(h2o_config, decode_waves), sizeof(h2o_state), offsetof(h2o_state, pos),
-         offsetof(h2o_config, decode_split));
+         offsetof(h2o_config, decode_split), offsetof(h2o_config, cache_dtype),
+         offsetof(h2o_state, v_scale));
   printf("%d\n", H2O_MAX_K);
   return 0;
 }''')
@@ -66,7 +67,8 @@ int main(void) {
     got = list(map(int, lines[0].split()))
     assert got == [ctypes.sizeof(B.h2o_config), B.h2o_config.scale.offset,
                    B.h2o_config.decode_waves.offset, ctypes.sizeof(B.h2o_state),
-                   B.h2o_state.pos.offset, B.h2o_config.decode_split.offset]
+                   B.h2o_state.pos.offset, B.h2o_config.decode_split.offset,
+                   B.h2o_config.cache_dtype.offset, B.h2o_state.v_scale.offset]
     assert int(lines[1]) == B.H2O_MAX_K
 
 
@@ -88,6 +90,9 @@ def test_status_strings():
     (dict(decode_waves=3), B.H2O_ERR_INVALID),
     (dict(decode_split=-1), B.H2O_ERR_INVALID),
     (dict(decode_split=65), B.H2O_ERR_INVALID),
+    (dict(cache_dtype=2), B.H2O_ERR_INVALID),
+    (dict(cache_dtype=1, kv_dtype=B.H2O_F32), B.H2O_ERR_INVALID),   # E4M3 cache takes bf16 inputs
+    (dict(cache_dtype=1), B.H2O_ERR_INVALID),                       # scales missing
     (dict(head_dim=80), B.H2O_ERR_UNSUPPORTED),
     (dict(head_dim=256), B.H2O_ERR_UNSUPPORTED),
     (dict(recent=4096, heavy=4097), B.H2O_ERR_UNSUPPORTED),
@@ -172,3 +177,10 @@ def test_decode_steps_position_overflow_is_rejected_up_front():
     assert k2.h2o_decode_steps(ctx, 9, FAKE, FAKE, FAKE, FAKE, None, None) == B.H2O_ERR_STATE
     assert k2.h2o_query(ctx) == (B.H2O_OK, INT32_MAX - 10, 8)
     k2.h2o_destroy(ctx)
+
+
+def test_e4m3_cache_needs_aligned_scales():
+    st, ctx = k2.h2o_create(cfg(cache_dtype=1), state(ks=FAKE, vs=FAKE))
+    assert st == B.H2O_OK
+    k2.h2o_destroy(ctx)
+    assert k2.h2o_create(cfg(cache_dtype=1), state(ks=FAKE + 4, vs=FAKE))[0] == B.H2O_ERR_INVALID

@@ -34,13 +34,14 @@ def _need_gpu():
     torch.cuda.synchronize()
 
 
-def run_workload(wl, n_units, steps, check_every=1, decode_waves=0, kv_every=64, decode_split=0):
+def run_workload(wl, n_units, steps, check_every=1, decode_waves=0, kv_every=64, decode_split=0,
+                 cache="input"):
     from parity import Harness, sample_units
     units = sample_units(wl, n_units)
     say(f"[parity] {wl.name} B={wl.batch} H={wl.heads} d={wl.head_dim} P={wl.prompt} "
         f"k={wl.k} ({wl.recent}+{wl.heavy}) {wl.kv_dtype} steps={steps} units={units[:6]}... "
-        f"waves={decode_waves} split={decode_split}")
-    hn = Harness(wl, units, steps, decode_waves=decode_waves, decode_split=decode_split)
+        f"waves={decode_waves} split={decode_split} cache={cache}")
+    hn = Harness(wl, units, steps, decode_waves=decode_waves, decode_split=decode_split, cache=cache)
     try:
         hn.prefill()
         stats = hn.run(check_every=check_every, kv_every=kv_every)
@@ -290,3 +291,27 @@ def test_decode_steps_equals_single_steps(name):
         cache.close()
     for a, b in zip(*res):
         assert torch.equal(a, b)
+
+
+# ---- E4M3 cache rows ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,units,steps", [("opt6.7b", 16, 256), ("opt30b", 8, 48),
+                                              ("neox20b", 4, 24), ("llama7b_stream", 4, 400)])
+def test_e4m3_cache_workloads(name, units, steps):
+    run_workload(WORKLOADS[name], units, steps, cache="e4m3", kv_every=8)
+
+
+BF16_EDGE = [w for w in EDGE if w.kv_dtype == "bf16"]
+
+
+@pytest.mark.parametrize("split", [1, 3])
+@pytest.mark.parametrize("wl", BF16_EDGE, ids=lambda w: w.name)
+def test_e4m3_cache_edge_cases(wl, split):
+    run_workload(wl, wl.units, wl.steps, kv_every=1, decode_split=split, cache="e4m3")
+
+
+@pytest.mark.parametrize("waves", [1, 8])
+def test_e4m3_cache_large_budget(waves):
+    wl = Workload(107, "large_budget_bf16", 1, 2, 128, 3000, 20, 1024, 1500, "bf16", "zipf",
+                  zipf_alpha=1.1)
+    run_workload(wl, 2, 20, decode_waves=waves, kv_every=5, cache="e4m3")
