@@ -63,13 +63,14 @@ def decode_source_hash():
     return h.hexdigest()
 
 
-def traffic_for(wl_name, waves):
-    """Measured HBM bytes per decode launch, if recorded for the current source."""
+def traffic_for(wl_name, waves, cache="input"):
+    """Measured HBM bytes per decode launch, if recorded for the current source
+    (records are keyed by workload, with "/e4m3" appended for an E4M3 cache)."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    ent = rec.get(wl_name)
+    ent = rec.get(wl_name if cache == "input" else f"{wl_name}/{cache}")
     if not ent or ent.get("source_sha256") != decode_source_hash() or ent.get("decode_waves") != waves:
         return None
     return ent.get("traffic_bytes_per_launch")
@@ -255,7 +256,7 @@ def main():
     mean_launch_ms = ms_per_step
     bytes_step = alg_bytes_per_step(wl, args.cache)
     achieved = bytes_step / (mean_launch_ms * 1e-3) / 1e9
-    traffic = traffic_for(wl.name, g["waves"]) if args.cache == "input" else None
+    traffic = traffic_for(wl.name, g["waves"], args.cache)
     line = {
         "metric": METRIC,
         "value": 1e3 / ms_per_step,

@@ -7,6 +7,7 @@ from .h2o_ref import (  # noqa: F401
     causal_attention,
     prefill_column_sums,
     prefill_keep,
+    prefill_output,
     prefill,
     decode_step,
     run_trace,

@@ -69,6 +69,14 @@ def prefill_column_sums(Q, K, scale):
     return causal_attention(Q, K, scale).sum(axis=0)
 
 
+def prefill_output(Q, K, V, scale):
+    """Attention output of every prompt position, O = A V with A the causal
+    attention matrix of the prompt (summary, "Algorithm / figure walkthrough",
+    step 1: the prompt is processed with full attention over its own prefix
+    before any eviction)."""
+    return causal_attention(Q, K, scale) @ np.asarray(V, dtype=np.float64)
+
+
 def prefill_keep(c, recent, heavy):
     """Positions kept after the prompt (sorted).
 

@@ -15,7 +15,7 @@ import pytest
 import torch
 import torch.nn.functional as F
 
-from oracle import (causal_attention, decode_step, prefill, prefill_column_sums,
+from oracle import (causal_attention, decode_step, prefill, prefill_column_sums, prefill_output,
                     prefill_keep, run_trace)
 from synth import WORKLOADS, gen
 
@@ -395,3 +395,28 @@ def test_e4m3_cache_keeps_definition_4_3():
         cur = set(res.members)
         assert len(cur) == wl.k and len(cur - prev) <= 1
         prev = cur
+
+
+# ---- prompt output ---------------------------------------------------------------
+
+@pytest.mark.parametrize("n,d,seed", [(1, 8, 11), (7, 16, 12), (40, 32, 13), (65, 64, 14)])
+def test_prefill_output_matches_library_causal_attention(n, d, seed):
+    # Full causal attention of the prompt (walkthrough step 1) is exactly what
+    # torch's scaled_dot_product_attention computes with is_causal=True.
+    Q, K, V = random_qkv(n, d, seed, spread=2.0)
+    scale = 1 / np.sqrt(d)
+    O = prefill_output(Q, K, V, scale)
+    np.testing.assert_allclose(O, sdpa(Q, K, V, scale, causal=True), rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_output_special_cases():
+    Q, K, V = random_qkv(12, 8, 15, spread=3.0)
+    O = prefill_output(Q, K, V, 0.5)
+    # the first position attends only to itself
+    np.testing.assert_allclose(O[0], V[0], rtol=0, atol=1e-14)
+    # constant values are reproduced (each attention row sums to one)
+    np.testing.assert_allclose(prefill_output(Q, K, np.full_like(V, 3.25), 0.5), 3.25, rtol=0, atol=1e-13)
+    # zero queries: position i averages the values of positions 0..i
+    Oz = prefill_output(np.zeros_like(Q), K, V, 0.5)
+    means = np.cumsum(V, axis=0) / np.arange(1, 13)[:, None]
+    np.testing.assert_allclose(Oz, means, rtol=0, atol=1e-13)
