@@ -162,7 +162,16 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     p1.record(stream)
     torch.cuda.synchronize()
     prefill_ms = p0.elapsed_time(p1)
-    del prompt
+    # The prefill that also returns the prompt's attention output, warm, then timed.
+    prompt_out = torch.empty((wl.batch, wl.heads, wl.prompt, wl.head_dim), dtype=torch.float32, device=dev)
+    cache.prefill(*prompt, out=prompt_out)
+    torch.cuda.synchronize()
+    p0.record(stream)
+    cache.prefill(*prompt, out=prompt_out)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    prefill_out_ms = p0.elapsed_time(p1)
+    del prompt, prompt_out
 
     for s in range(warmup):
         cache.step(dq[s], dk[s], dv[s])
@@ -196,7 +205,7 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     if waves == 0:
         waves_used = decode_waves_auto(wl.units)
     cache.close()
-    return dict(region_ms=region_ms, prefill_ms=prefill_ms, waves=waves_used,
+    return dict(region_ms=region_ms, prefill_ms=prefill_ms, prefill_out_ms=prefill_out_ms, waves=waves_used,
                 device=torch.cuda.get_device_name(0))
 
 
@@ -294,6 +303,12 @@ def main():
             "ms": g["prefill_ms"],
             "qk_tflops": prefill_flops(wl) / (g["prefill_ms"] * 1e-3) / 1e12,
             "peak_tflops": PEAK_BF16_TFLOPS if wl.kv_dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS,
+            "with_output": {
+                "ms": g["prefill_out_ms"],
+                # causal QK^T and PV: each P(P+1)/2 dot products of length d per unit
+                "tflops": 2 * prefill_flops(wl) / (g["prefill_out_ms"] * 1e-3) / 1e12,
+                "out_bytes": wl.units * wl.prompt * wl.head_dim * 4,
+            },
         },
         "cpu_baseline": cpu,
         "device": g["device"],

@@ -127,6 +127,19 @@ h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** o
 h2o_status h2o_prefill(h2o_ctx* ctx, const void* q, const void* k, const void* v,
                        int32_t prompt_len, void* stream);
 
+/* h2o_prefill that also returns the attention output of every prompt position
+ * (summary, "Algorithm / figure walkthrough", step 1: the prompt is processed
+ * with full causal attention over its own prefix before any eviction):
+ * out[b, h, i, :] = sum_{j <= i} softmax_j(scale * q_i . k_j) v_j.  out:
+ * [B, H, prompt_len, d] float32, device, 16-byte aligned, written whole.  The
+ * cache state afterwards is the one h2o_prefill leaves.  For bf16 inputs the
+ * probabilities enter the value product rounded to bf16 (relative error at most
+ * 2^-8 per weight); the row statistics and sums stay float32.  out == NULL is
+ * h2o_prefill.  Same errors as h2o_prefill, plus H2O_ERR_INVALID for a
+ * misaligned out.  Three kernels on `stream`. */
+h2o_status h2o_prefill_with_output(h2o_ctx* ctx, const void* q, const void* k, const void* v,
+                                   int32_t prompt_len, float* out, void* stream);
+
 /* One decode step for every unit (summary, "Algorithm / figure walkthrough",
  * steps 2-4; "The mechanism", H2O eviction).  q, k_new, v_new: [B, H, d]
  * kv_dtype, device, the token at the current position t.  out: [B, H, d]

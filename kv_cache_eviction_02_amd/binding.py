@@ -78,6 +78,8 @@ def load_library(path=LIB_PATH):
     lib.h2o_create.restype = ctypes.c_int
     lib.h2o_prefill.argtypes = [vp, vp, vp, vp, i32, vp]
     lib.h2o_prefill.restype = ctypes.c_int
+    lib.h2o_prefill_with_output.argtypes = [vp, vp, vp, vp, i32, vp, vp]
+    lib.h2o_prefill_with_output.restype = ctypes.c_int
     lib.h2o_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.h2o_decode_step.restype = ctypes.c_int
     lib.h2o_decode_steps.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
@@ -112,6 +114,10 @@ def h2o_create(cfg: h2o_config, state: h2o_state):
 
 def h2o_prefill(ctx, q, k, v, prompt_len, stream):
     return load_library().h2o_prefill(ctx, q, k, v, prompt_len, stream)
+
+
+def h2o_prefill_with_output(ctx, q, k, v, prompt_len, out, stream):
+    return load_library().h2o_prefill_with_output(ctx, q, k, v, prompt_len, out, stream)
 
 
 def h2o_decode_step(ctx, q, k_new, v_new, out, evicted_pos, stream):
@@ -204,11 +210,27 @@ class H2OCache:
                              f"got {x.dtype} {tuple(x.shape)} on {x.device}")
         return x.data_ptr()
 
-    def prefill(self, q, k, v):
+    def _output(self, x, shape, dtype, name):
+        if x.dtype != dtype or tuple(x.shape) != shape or not x.is_contiguous() or x.device != self.device:
+            raise ValueError(f"{name}: expected contiguous {dtype} {shape} on {self.device}, "
+                             f"got {x.dtype} {tuple(x.shape)} on {x.device}")
+        return x.data_ptr()
+
+    def prefill(self, q, k, v, output=False, out=None):
+        """Seed the cache from a prompt [B, H, P, d].  With output=True (or an
+        out tensor) also returns the prompt's attention output [B, H, P, d]
+        float32."""
         P = q.shape[2]
         shape = (self.batch, self.heads, P, self.head_dim)
         ptrs = [self._input(x, shape, n) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
-        _check(h2o_prefill(self.ctx, *ptrs, P, self._stream()), "h2o_prefill")
+        if not output and out is None:
+            _check(h2o_prefill(self.ctx, *ptrs, P, self._stream()), "h2o_prefill")
+            return None
+        if out is None:
+            out = self.torch.empty(shape, dtype=self.torch.float32, device=self.device)
+        optr = self._output(out, shape, self.torch.float32, "out")
+        _check(h2o_prefill_with_output(self.ctx, *ptrs, P, optr, self._stream()), "h2o_prefill_with_output")
+        return out
 
     def step(self, q, k_new, v_new, out=None, evicted=None):
         """One decode step; returns (out [B, H, d] float32, evicted [B, H] int32)."""
@@ -216,8 +238,9 @@ class H2OCache:
         ptrs = [self._input(x, shape, n) for x, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"))]
         out = self.out if out is None else out
         evicted = self.evicted if evicted is None else evicted
-        _check(h2o_decode_step(self.ctx, *ptrs, out.data_ptr(), evicted.data_ptr(), self._stream()),
-               "h2o_decode_step")
+        optr = self._output(out, shape, self.torch.float32, "out")
+        eptr = self._output(evicted, shape[:2], self.torch.int32, "evicted")
+        _check(h2o_decode_step(self.ctx, *ptrs, optr, eptr, self._stream()), "h2o_decode_step")
         return out, evicted
 
     def steps(self, q, k_new, v_new, out=None, evicted=None):
@@ -231,8 +254,9 @@ class H2OCache:
             out = torch.empty(shape, dtype=torch.float32, device=self.device)
         if evicted is None:
             evicted = torch.empty(shape[:3], dtype=torch.int32, device=self.device)
-        _check(h2o_decode_steps(self.ctx, n, *ptrs, out.data_ptr(), evicted.data_ptr(), self._stream()),
-               "h2o_decode_steps")
+        optr = self._output(out, shape, torch.float32, "out")
+        eptr = self._output(evicted, shape[:3], torch.int32, "evicted")
+        _check(h2o_decode_steps(self.ctx, n, *ptrs, optr, eptr, self._stream()), "h2o_decode_steps")
         return out, evicted
 
     def position(self):

@@ -127,8 +127,13 @@ h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** o
 
 h2o_status h2o_prefill(h2o_ctx* ctx, const void* q, const void* k, const void* v,
                        int32_t prompt_len, void* stream) {
+  return h2o_prefill_with_output(ctx, q, k, v, prompt_len, nullptr, stream);
+}
+
+h2o_status h2o_prefill_with_output(h2o_ctx* ctx, const void* q, const void* k, const void* v,
+                                   int32_t prompt_len, float* out, void* stream) {
   if (!ctx || !q || !k || !v) return H2O_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return H2O_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (out && !aligned16(out))) return H2O_ERR_INVALID;
   if (prompt_len < 1 || prompt_len > ctx->cfg.max_prompt) return H2O_ERR_INVALID;
   const size_t units = (size_t)ctx->cfg.batch * ctx->cfg.heads;
   if ((int64_t)((prompt_len + 63) / 64) * (int64_t)units > INT32_MAX) return H2O_ERR_INVALID;
@@ -144,6 +149,7 @@ h2o_status h2o_prefill(h2o_ctx* ctx, const void* q, const void* k, const void* v
   a.v_scale = ctx->st.v_scale;
   a.row_lse = ctx->scratch;
   a.colsum = ctx->scratch + units * ctx->stride;
+  a.out = out;
   a.units = (int32_t)units;
   a.stride = ctx->stride;
   a.P = prompt_len;

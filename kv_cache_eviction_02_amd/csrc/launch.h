@@ -46,6 +46,7 @@ struct PrefillArgs {
   float* v_scale;
   float* row_lse;      // scratch [U, stride]: per query row, log2 of the softmax denominator (log2 domain)
   float* colsum;       // scratch [U, stride]: accumulated attention per prompt position
+  float* out;          // [U, P, d] float32 prompt attention output, or null
   int32_t units;
   int32_t stride;      // scratch row stride in floats: max_prompt rounded up to 16
   int32_t P;

@@ -199,6 +199,244 @@ __global__ __launch_bounds__(kWaves * 64) void rowstats_kernel(PrefillArgs a, in
   }
 }
 
+// ---- prompt attention output --------------------------------------------------
+//
+// O_i = sum_{j <= i} softmax_i(s_ij) v_j for every prompt row (the full causal
+// attention the prompt is processed with before any eviction), computed in the
+// sweep that owns query rows, which then also writes lse_i for the column sums.
+// Keys and values go through LDS in chunks of 32 rows shared by the block's four
+// wavefronts; each wavefront owns 32 queries as two fixed 16-row subtiles.
+//   S^T tiles: acc[i] = s(key 16*sub + 4*(l/16) + i, query l%16), as in rowstats.
+//   O^T tiles: D[col][query] = sum_key V[key][col] P[query][key] on the same
+//              MFMA.  Lane (g, n) passes the eight probabilities it holds for
+//              query n (chunk rows 16*(e/4) + 4g + e%4, e = 0..7) as the B
+//              operand; the A operand carries the same eight rows of column
+//              16*dt + n.  For bf16 two ds_read_b64_tr_b16 fetch them from the
+//              row-major V chunk: within each 16-lane block that instruction
+//              returns element e of lane L from element L%4 of lane 4e + L/4, so
+//              lane s of block g addresses row 4g + s/4, column 16*dt + 4*(s%4).
+// The four lane groups holding a query share its running maximum, so the 32
+// probabilities of a chunk enter one MFMA.  The maximum is raised only when a
+// chunk exceeds it by more than kLazy (log2 units): unnormalised probabilities
+// stay below 2^kLazy and most chunks need no rescale of the accumulators.
+template <typename T, int D>
+struct AttendTile {
+  static constexpr int QS = 2;                        // fixed query subtiles per wavefront
+  static constexpr int ROWS = QS * kTile;             // queries per wavefront
+  static constexpr int BQ = kWaves * ROWS;            // queries per block
+  static constexpr int KC = 2 * kTile;                // keys per chunk
+  static constexpr int ROWB = D * Elem<T>::kBytes;
+  static constexpr int KSTR = ROWB + 16;              // K rows in LDS: 16 rows of one subtile hit distinct banks
+  static constexpr int VSTR = ROWB + 32;              // V rows in LDS: 8 rows x 32 bytes hit distinct banks
+  static constexpr int PIECES = KC * ROWB / 16;       // 16-byte pieces of a K (or V) chunk
+  static constexpr int PER_T = (PIECES + kWaves * 64 - 1) / (kWaves * 64);
+  static constexpr int NDT = D / 16;                  // 16-wide output column tiles
+  static constexpr int BUF = KC * (KSTR + VSTR);      // bytes of one K + V chunk
+  static constexpr int NBUF = 2 * BUF <= 60 * 1024 ? 2 : 1;
+};
+
+constexpr float kLazy = 8.f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Rows row0 .. row0 + 15 of a K chunk in LDS as MFMA operands (lane: row l%16, quarter l/16).
+template <typename T, int D>
+__device__ inline void load_lds_frag(Frag<T, D>& f, const char* base, int row0, int stride, int lane) {
+  const char* p = base + (row0 + (lane & 15)) * stride + (lane >> 4) * Frag<T, D>::kBytes;
+#pragma unroll
+  for (int i = 0; i < Frag<T, D>::kChunks; ++i) f.c[i] = *reinterpret_cast<const uint4*>(p + 16 * i);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void attend_kernel(
+    PrefillArgs a, int stride, int nblk) {
+  using AT = AttendTile<T, D>;
+  constexpr int QS = AT::QS;
+  constexpr int NDT = AT::NDT;
+  constexpr float kLow = -1.0e30f;
+  __shared__ __attribute__((aligned(16))) char smem[AT::NBUF * AT::BUF];
+
+  const int id = xcd_local_block(nblk * a.units);
+  const int unit = id / nblk;
+  const int blk = nblk - 1 - id % nblk;  // longest rows first
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int P = a.P;
+  const int qb0 = blk * AT::BQ;
+  const int qw0 = qb0 + (tid >> 6) * AT::ROWS;      // first query of this wavefront
+  const int qw_last = min(qw0 + AT::ROWS, P) - 1;   // < qw0 when the wavefront has no query
+  const int kend = min(P, qb0 + AT::BQ);            // keys the block needs
+  const int nch = (kend + AT::KC - 1) / AT::KC;
+  const char* Qb = (const char*)a.pq + (size_t)unit * P * AT::ROWB;
+  const char* Kb = (const char*)a.pk + (size_t)unit * P * AT::ROWB;
+  const char* Vb = (const char*)a.pv + (size_t)unit * P * AT::ROWB;
+  const float sc = a.scale_log2;
+
+  Frag<T, D> fq[QS];
+#pragma unroll
+  for (int q = 0; q < QS; ++q) fq[q].load(Qb, qw0 + q * kTile, P, lane);
+  float m[QS], l[QS];
+  f32x4 o[QS][NDT];
+#pragma unroll
+  for (int q = 0; q < QS; ++q) {
+    m[q] = kLow;
+    l[q] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[q][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  uint4 rk[AT::PER_T], rv[AT::PER_T];
+  auto fetch = [&](int ch) {
+#pragma unroll
+    for (int u = 0; u < AT::PER_T; ++u) {
+      const int idx = tid + u * kWaves * 64;
+      const int key = ch * AT::KC + idx / (AT::ROWB / 16);
+      const int c16 = idx % (AT::ROWB / 16);
+      const bool in = idx < AT::PIECES && key < kend;
+      rk[u] = in ? load16(Kb + (size_t)key * AT::ROWB + c16 * 16) : make_uint4(0, 0, 0, 0);
+      rv[u] = in ? load16(Vb + (size_t)key * AT::ROWB + c16 * 16) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stash = [&](int b) {
+    char* kl = smem + b * AT::BUF;
+    char* vl = kl + AT::KC * AT::KSTR;
+#pragma unroll
+    for (int u = 0; u < AT::PER_T; ++u) {
+      const int idx = tid + u * kWaves * 64;
+      if (idx < AT::PIECES) {
+        const int row = idx / (AT::ROWB / 16);
+        const int c16 = idx % (AT::ROWB / 16);
+        *reinterpret_cast<uint4*>(kl + row * AT::KSTR + c16 * 16) = rk[u];
+        *reinterpret_cast<uint4*>(vl + row * AT::VSTR + c16 * 16) = rv[u];
+      }
+    }
+  };
+
+  auto compute = [&](int ch, const char* kl, const char* vl) {
+    const int c0 = ch * AT::KC;
+    f32x4 s[2][QS];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      Frag<T, D> fk;
+      load_lds_frag<T, D>(fk, kl, sub * kTile, AT::KSTR, lane);
+#pragma unroll
+      for (int q = 0; q < QS; ++q) s[sub][q] = tile_dot<T, D>(fk, fq[q]);
+    }
+    if (c0 + AT::KC - 1 > qw0 || c0 + AT::KC > P) {  // uniform: some key is masked
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int q = 0; q < QS; ++q) {
+          const int qi = qw0 + q * kTile + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kj = c0 + sub * kTile + 4 * g + i;
+            s[sub][q][i] = (kj <= qi && kj < P) ? s[sub][q][i] : -INFINITY;
+          }
+        }
+    }
+    float alpha[QS];
+    bool raise_any = false;
+    f32x4 p[2][QS];
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+        mx = fmaxf(mx, fmaxf(fmaxf(s[sub][q][0], s[sub][q][1]), fmaxf(s[sub][q][2], s[sub][q][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float ms = mx * sc;
+      const bool raise = ms > m[q] + kLazy;
+      const float mn = raise ? ms : m[q];
+      alpha[q] = fast_exp2(m[q] - mn);
+      raise_any |= raise;
+      m[q] = mn;
+      float add = 0.f;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[sub][q][i] = fast_exp2(fmaf(s[sub][q][i], sc, -mn));
+          add += p[sub][q][i];
+        }
+      l[q] = fmaf(l[q], alpha[q], add);
+    }
+    if (__any(raise_any)) {
+#pragma unroll
+      for (int q = 0; q < QS; ++q)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[q][dt] *= alpha[q];
+    }
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 pb[QS];
+#pragma unroll
+      for (int q = 0; q < QS; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[q][e] = (__bf16)p[e >> 2][q][e & 3];
+      const int s16 = lane & 15;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const char* v0 = vl + (4 * g + (s16 >> 2)) * AT::VSTR + (16 * dt + 4 * (s16 & 3)) * 2;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)v0);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v0 + kTile * AT::VSTR));
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
+#pragma unroll
+        for (int q = 0; q < QS; ++q)
+          o[q][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[q], o[q][dt], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float va = *reinterpret_cast<const float*>(
+                vl + (sub * kTile + 4 * g + i) * AT::VSTR + (16 * dt + (lane & 15)) * 4);
+#pragma unroll
+            for (int q = 0; q < QS; ++q)
+              o[q][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va, p[sub][q][i], o[q][dt], 0, 0, 0);
+          }
+    }
+  };
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    if (ch + 1 < nch) fetch(ch + 1);
+    const char* kl = smem + (ch % AT::NBUF) * AT::BUF;
+    if (ch * AT::KC <= qw_last) compute(ch, kl, kl + AT::KC * AT::KSTR);  // uniform
+    if (AT::NBUF == 1) __syncthreads();
+    if (ch + 1 < nch) stash((ch + 1) % AT::NBUF);
+    __syncthreads();
+  }
+
+  if (qw0 >= P) return;
+#pragma unroll
+  for (int q = 0; q < QS; ++q) {
+    float lt = l[q];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const int qi = qw0 + q * kTile + (lane & 15);
+    if (qi < P) {
+      const float inv = 1.f / lt;
+      float* orow = a.out + ((size_t)unit * P + qi) * D + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const f32x4 v = o[q][dt] * inv;
+        *reinterpret_cast<float4*>(orow + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (g == 0) a.row_lse[(size_t)unit * stride + qi] = m[q] + __log2f(lt);
+    }
+  }
+}
+
 // Column sums c_j = sum_{i >= j} exp2(s_ij - lse_i).  A wavefront owns
 // kFixed*16 keys and walks the query subtiles from its first key to the end
 // of the prompt in a fixed order, so the sums are deterministic.
@@ -458,7 +696,14 @@ hipError_t launch_prefill_td(const PrefillArgs& a, int stride, hipStream_t s) {
   constexpr int rows_per_block = kWaves * rows_per_wave<T>();
   const int nblk = (a.P + rows_per_block - 1) / rows_per_block;
   const dim3 grid((unsigned)(nblk * a.units));
-  hipLaunchKernelGGL((rowstats_kernel<T, D>), grid, dim3(kWaves * 64), 0, s, a, stride, nblk);
+  if (a.out) {
+    constexpr int bq = AttendTile<T, D>::BQ;
+    const int nblk_o = (a.P + bq - 1) / bq;
+    hipLaunchKernelGGL((attend_kernel<T, D>), dim3((unsigned)(nblk_o * a.units)), dim3(kWaves * 64), 0, s,
+                       a, stride, nblk_o);
+  } else {
+    hipLaunchKernelGGL((rowstats_kernel<T, D>), grid, dim3(kWaves * 64), 0, s, a, stride, nblk);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((colsum_kernel<T, D>), grid, dim3(kWaves * 64), 0, s, a, stride, nblk);

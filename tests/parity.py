@@ -16,15 +16,20 @@ Tolerances:
     GPU's own score += p is up to half an ulp);
   * prefill: scores as above; the kept set exact except for positions whose
     oracle score lies within tau_pre = max(1e-5, 1e-4 * c_h) of the h-th
-    largest score c_h (fp32 column sums over up to P terms).
+    largest score c_h (fp32 column sums over up to P terms);
+  * prompt attention output, per element: |o_gpu - o_ref| <= e * (A|V|)_ic + 1e-6
+    where (A|V|)_ic = sum_j a_ij |v_jc| from the oracle's attention matrix and
+    e = 2^-8 + 2e-4 for bf16 inputs (the probabilities enter the value product
+    rounded to bf16: relative error at most 2^-8 each, plus float32 logits,
+    exp2 and sums), e = 2e-4 for float32 inputs.
 """
 import math
 
 import numpy as np
 import torch
 
-from oracle import (decode_step, dequantize_row_e4m3, members_from_slots, prefill,
-                    quantize_row_e4m3)
+from oracle import (causal_attention, decode_step, dequantize_row_e4m3, members_from_slots,
+                    prefill, quantize_row_e4m3)
 from synth import gen
 from synth.stage import stage_decode, stage_prompt
 
@@ -45,11 +50,14 @@ class Stats:
         self.max_out_rel = 0.0
         self.max_score_rel = 0.0
         self.prefill_near_ties = 0
+        self.prompt_out_rows = 0
+        self.prompt_out_err_over_tol = 0.0
 
     def __repr__(self):
         return (f"Stats(steps={self.steps}, near_ties={self.near_ties}, "
                 f"prefill_near_ties={self.prefill_near_ties}, max_out_rel={self.max_out_rel:.3g}, "
-                f"max_score_rel={self.max_score_rel:.3g})")
+                f"max_score_rel={self.max_score_rel:.3g}, prompt_out_rows={self.prompt_out_rows}, "
+                f"prompt_out_err_over_tol={self.prompt_out_err_over_tol:.3g})")
 
 
 def sample_units(wl, n, seed=0):
@@ -112,12 +120,33 @@ class Harness:
 
     # ---- prefill -------------------------------------------------------------
 
-    def prefill(self):
+    def prefill(self, output=False):
         q, k, v = stage_prompt(self.wl, self.device)
-        self.cache.prefill(q, k, v)
+        O = self.cache.prefill(q, k, v, output=output)
         torch.cuda.synchronize()
         del q, k, v
+        if output:
+            U, P, d = self.wl.units, self.wl.prompt, self.wl.head_dim
+            O = O.view(U, P, d).index_select(0, self.idx).cpu().numpy()
+            self.check_prompt_output(O)
         self.check_prefill()
+
+    def check_prompt_output(self, O):
+        wl = self.wl
+        P = wl.prompt
+        e = 2.0 ** -8 + 2e-4 if wl.kv_dtype == "bf16" else 2e-4
+        for i, u in enumerate(self.units):
+            Q, K, V = self.vals[u]
+            A = causal_attention(Q[:P], K[:P], wl.scale)
+            ref = A @ V[:P]
+            tol = e * (A @ np.abs(V[:P])) + 1e-6
+            err = np.abs(O[i].astype(np.float64) - ref)
+            assert np.all(np.isfinite(O[i])), u
+            worst = np.unravel_index(np.argmax(err / tol), err.shape)
+            assert np.all(err <= tol), (u, worst, O[i][worst], ref[worst], tol[worst])
+            self.stats.prompt_out_rows += P
+            self.stats.prompt_out_err_over_tol = max(self.stats.prompt_out_err_over_tol,
+                                                     float(np.max(err / tol)))
 
     def check_prefill(self):
         wl = self.wl

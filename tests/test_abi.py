@@ -37,7 +37,8 @@ def state(k=FAKE, v=FAKE, s=FAKE, p=FAKE, ks=None, vs=None):
 def test_library_exports_every_header_function():
     lib = B.load_library()
     names = header_functions()
-    assert names == sorted(["h2o_create", "h2o_prefill", "h2o_decode_step", "h2o_decode_steps",
+    assert names == sorted(["h2o_create", "h2o_prefill", "h2o_prefill_with_output",
+                            "h2o_decode_step", "h2o_decode_steps",
                             "h2o_query", "h2o_destroy", "h2o_status_string"])
     for n in names:
         assert hasattr(lib, n), n
@@ -132,6 +133,8 @@ def test_call_order_and_argument_checks_without_device_work():
         assert k2.h2o_prefill(ctx, FAKE, FAKE, FAKE, 1, None) == B.H2O_ERR_INVALID
         assert k2.h2o_prefill(ctx, FAKE, FAKE, FAKE, 0, None) == B.H2O_ERR_INVALID
         assert k2.h2o_prefill(ctx, 0, FAKE, FAKE, 1, None) == B.H2O_ERR_INVALID
+        assert k2.h2o_prefill_with_output(ctx, FAKE, FAKE, FAKE, 0, FAKE, None) == B.H2O_ERR_INVALID
+        assert k2.h2o_prefill_with_output(ctx, FAKE, FAKE, FAKE, 1, FAKE + 4, None) == B.H2O_ERR_INVALID
         assert k2.h2o_decode_steps(ctx, 4, FAKE, FAKE, FAKE, FAKE, None, None) == B.H2O_ERR_STATE
         assert k2.h2o_decode_steps(ctx, 0, FAKE, FAKE, FAKE, FAKE, None, None) == B.H2O_ERR_INVALID
         assert k2.h2o_query(ctx) == (B.H2O_OK, 0, 0)   # unchanged by failed calls

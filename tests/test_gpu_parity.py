@@ -35,15 +35,15 @@ def _need_gpu():
 
 
 def run_workload(wl, n_units, steps, check_every=1, decode_waves=0, kv_every=64, decode_split=0,
-                 cache="input"):
+                 cache="input", prompt_output=False):
     from parity import Harness, sample_units
     units = sample_units(wl, n_units)
     say(f"[parity] {wl.name} B={wl.batch} H={wl.heads} d={wl.head_dim} P={wl.prompt} "
         f"k={wl.k} ({wl.recent}+{wl.heavy}) {wl.kv_dtype} steps={steps} units={units[:6]}... "
-        f"waves={decode_waves} split={decode_split} cache={cache}")
+        f"waves={decode_waves} split={decode_split} cache={cache} prompt_output={prompt_output}")
     hn = Harness(wl, units, steps, decode_waves=decode_waves, decode_split=decode_split, cache=cache)
     try:
-        hn.prefill()
+        hn.prefill(output=prompt_output)
         stats = hn.run(check_every=check_every, kv_every=kv_every)
     finally:
         hn.close()
@@ -315,3 +315,29 @@ def test_e4m3_cache_large_budget(waves):
     wl = Workload(107, "large_budget_bf16", 1, 2, 128, 3000, 20, 1024, 1500, "bf16", "zipf",
                   zipf_alpha=1.1)
     run_workload(wl, 2, 20, decode_waves=waves, kv_every=5, cache="e4m3")
+
+
+# ---- prompt attention output of the prefill ------------------------------------------
+
+@pytest.mark.parametrize("name,units,steps", [("tiny_fp32", 2, 16), ("opt6.7b", 8, 16), ("opt30b", 6, 8),
+                                              ("neox20b", 3, 4), ("llama7b_stream", 4, 16)])
+def test_prompt_output_workloads(name, units, steps):
+    stats = run_workload(WORKLOADS[name], units, steps, kv_every=4, prompt_output=True)
+    assert stats.prompt_out_rows == len(sample_units_for(name, units)) * WORKLOADS[name].prompt
+
+
+def sample_units_for(name, n):
+    from parity import sample_units
+    return sample_units(WORKLOADS[name], n)
+
+
+@pytest.mark.parametrize("wl", EDGE, ids=lambda w: w.name)
+def test_prompt_output_edge_cases(wl):
+    run_workload(wl, wl.units, 8, kv_every=1, prompt_output=True)
+
+
+def test_prompt_output_large_prompt_and_e4m3_cache():
+    wl = Workload(107, "large_budget_bf16", 1, 2, 128, 3000, 20, 1024, 1500, "bf16", "zipf",
+                  zipf_alpha=1.1)
+    run_workload(wl, 2, 8, kv_every=4, prompt_output=True)
+    run_workload(wl, 2, 8, kv_every=4, prompt_output=True, cache="e4m3")
