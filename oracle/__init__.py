@@ -8,6 +8,8 @@ from .h2o_ref import (  # noqa: F401
     prefill_column_sums,
     prefill_keep,
     prefill_output,
+    prefill_scores,
+    POLICIES,
     prefill,
     decode_step,
     run_trace,

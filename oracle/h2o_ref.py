@@ -38,6 +38,20 @@ Readings taken where the pages leave a step open:
 * Prefill scores are the column sums of the exact causal attention of the whole
   prompt; if the prompt exceeds k, the newest r prompt positions are kept and
   the h best of the rest by that order.
+
+Ablation policies the pages contrast with H2O (summary, "Prior limits" and
+"Limitations"), each a change of one step of the same loop:
+
+* "static" (static Top-K without heavy-hitter dynamics): the heavy set is
+  picked once; after the cache is full the victim is always the position that
+  leaves the protected window, so the heavy members never change and the rest
+  behaves as a sliding window.  Scores are still accumulated (they decide
+  nothing).  While the cache is filling, positions are admitted as under H2O.
+* "naive" (per-step Top-K without accumulation): a member's score is only the
+  weight it received at the current step; the prefill ranks the prompt
+  positions by the attention of the last prompt token alone.
+* heavy-only is H2O with recent = 0: no protected window, so the token being
+  decoded is a candidate for eviction too (positions <= t - 0).
 """
 from collections import namedtuple
 
@@ -93,18 +107,33 @@ def prefill_keep(c, recent, heavy):
     return sorted(ranked[:heavy]) + list(range(n - recent, n))
 
 
-def prefill(Q, K, recent, heavy, scale):
-    """Seed the cache from the prompt.  Returns ({position: score}, c)."""
-    c = prefill_column_sums(Q, K, scale)
+POLICIES = ("h2o", "static", "naive")
+
+
+def prefill_scores(Q, K, scale, policy="h2o"):
+    """Score of every prompt position after the prompt: the causal column sums
+    (accumulated attention), or for the naive policy the attention the last
+    prompt token gives each position."""
+    if policy == "naive":
+        return causal_attention(Q, K, scale)[-1]
+    if policy not in POLICIES:
+        raise ValueError(policy)
+    return prefill_column_sums(Q, K, scale)
+
+
+def prefill(Q, K, recent, heavy, scale, policy="h2o"):
+    """Seed the cache from the prompt.  Returns ({position: score}, scores)."""
+    c = prefill_scores(Q, K, scale, policy)
     return {j: float(c[j]) for j in prefill_keep(c, recent, heavy)}, c
 
 
-def decode_step(members, t, q, K, V, recent, heavy, scale, K_cached=None, V_cached=None):
-    """One H2O decode step for the token at absolute position t.
+def decode_step(members, t, q, K, V, recent, heavy, scale, K_cached=None, V_cached=None,
+                policy="h2o"):
+    """One decode step for the token at absolute position t.
 
-    ``members`` maps each cached position (< t) to its accumulated score.  K and
-    V are indexable by absolute position and hold rows for every member and for
-    t itself.  When the cache stores rows in a lossy form, K_cached / V_cached
+    ``members`` maps each cached position (< t) to its score.  K and V are
+    indexable by absolute position and hold rows for every member and for t
+    itself.  When the cache stores rows in a lossy form, K_cached / V_cached
     give the rows as stored (indexable by position) and are used for the
     members; the token being decoded always attends with its exact row.
     Returns StepResult(out, evicted, members after the step, the softmax weight
@@ -112,11 +141,15 @@ def decode_step(members, t, q, K, V, recent, heavy, scale, K_cached=None, V_cach
 
     Order of work (summary, "Algorithm / figure walkthrough", steps 2-4):
       1. attend over the members and the new token;
-      2. add every weight into that position's score; the new token enters with
-         its own weight;
-      3. if the cache now exceeds k = recent + heavy, evict the candidate
-         (position <= t - recent) with the smallest score, older first on ties.
+      2. add every weight into that position's score (naive policy: the score
+         becomes the weight); the new token enters with its own weight;
+      3. if the cache now exceeds k = recent + heavy, evict among the
+         candidates (positions <= t - recent): the smallest score, older first
+         on ties; under the static policy the newest candidate, the position
+         leaving the protected window.
     """
+    if policy not in POLICIES:
+        raise ValueError(policy)
     q = np.asarray(q, dtype=np.float64)
     attended = sorted(members) + [t]
     Kc = K if K_cached is None else K_cached
@@ -128,26 +161,30 @@ def decode_step(members, t, q, K, V, recent, heavy, scale, K_cached=None, V_cach
     p = w / w.sum()
     out = p @ Va
 
-    after = {j: members[j] + float(p[i]) for i, j in enumerate(attended[:-1])}
+    keep_old = 0.0 if policy == "naive" else 1.0
+    after = {j: keep_old * members[j] + float(p[i]) for i, j in enumerate(attended[:-1])}
     after[t] = float(p[-1])
 
     evicted = None
     if len(after) > recent + heavy:
         candidates = [j for j in after if j <= t - recent]
-        evicted = min(candidates, key=lambda j: (after[j], j))
+        if policy == "static":
+            evicted = max(candidates)
+        else:
+            evicted = min(candidates, key=lambda j: (after[j], j))
         del after[evicted]
     weights = {j: float(p[i]) for i, j in enumerate(attended)}
     return StepResult(out, evicted, after, weights, attended)
 
 
-def run_trace(Q, K, V, prompt, steps, recent, heavy, scale, cache="exact"):
+def run_trace(Q, K, V, prompt, steps, recent, heavy, scale, cache="exact", policy="h2o"):
     """Prefill on positions [0, prompt) then ``steps`` decode steps.
 
     Q, K, V hold rows for positions [0, prompt + steps).  cache="e4m3" stores
     every cached row as per-row-scaled E4M3 (quantize_row_e4m3); the prefill
     scores still come from the exact prompt.  Returns (members after prefill,
-    prompt column sums, [StepResult per step])."""
-    members, c = prefill(Q[:prompt], K[:prompt], recent, heavy, scale)
+    prompt scores, [StepResult per step])."""
+    members, c = prefill(Q[:prompt], K[:prompt], recent, heavy, scale, policy)
     Kc = Vc = None
     if cache == "e4m3":
         Kc = np.asarray([dequantize_row_e4m3(*quantize_row_e4m3(row)) for row in K])
@@ -158,7 +195,7 @@ def run_trace(Q, K, V, prompt, steps, recent, heavy, scale, cache="exact"):
     results = []
     for s in range(steps):
         t = prompt + s
-        res = decode_step(members, t, Q[t], K, V, recent, heavy, scale, Kc, Vc)
+        res = decode_step(members, t, Q[t], K, V, recent, heavy, scale, Kc, Vc, policy)
         results.append(res)
         members = res.members
     return seeded, c, results

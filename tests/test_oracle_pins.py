@@ -16,6 +16,7 @@ import torch
 import torch.nn.functional as F
 
 from oracle import (causal_attention, decode_step, prefill, prefill_column_sums, prefill_output,
+                    prefill_scores,
                     prefill_keep, run_trace)
 from synth import WORKLOADS, gen
 
@@ -420,3 +421,135 @@ def test_prefill_output_special_cases():
     Oz = prefill_output(np.zeros_like(Q), K, V, 0.5)
     means = np.cumsum(V, axis=0) / np.arange(1, 13)[:, None]
     np.testing.assert_allclose(Oz, means, rtol=0, atol=1e-13)
+
+
+# ---- ablation policies (summary, "Prior limits" and "Limitations") -------------
+
+def band_mask(n, allowed):
+    """Boolean attention mask: row i may attend the positions allowed(i)."""
+    m = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        m[i, list(allowed(i))] = True
+    return m
+
+
+def test_heavy_only_uniform_attention_closed_form():
+    # r = 0, q = 0: every attended weight is 1/(n+1).  The prompt keeps the h
+    # oldest positions (largest harmonic column sums); once full, the new token's
+    # weight 1/(h+1) is below every member's score, so it is evicted at once.
+    P, T, h, d = 40, 30, 8, 8
+    rng = np.random.default_rng(21)
+    N = P + T
+    Q = np.zeros((N, d))
+    K, V = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    seeded, _, steps = run_trace(Q, K, V, P, T, 0, h, 0.5)
+    assert sorted(seeded) == list(range(h))
+    for s, res in enumerate(steps):
+        t = P + s
+        assert res.evicted == t
+        assert sorted(res.members) == list(range(h))
+        np.testing.assert_allclose(res.out, V[list(range(h)) + [t]].mean(0), rtol=1e-12, atol=1e-13)
+
+
+def test_heavy_only_keeps_definition_4_3_and_admits_strong_tokens():
+    # Heavy-only traces: |S| = k once full, at most one change per step.  Every
+    # third token's key is aligned with its query, so its own weight is close to
+    # one and beats the weakest member; the others are evicted at once.
+    P, T, h, d = 12, 60, 6, 8
+    Q, K, V = random_qkv(P + T, d, 22, spread=1.0)
+    for t in range(P, P + T, 3):
+        K[t] = 3.0 * Q[t]
+    seeded, _, steps = run_trace(Q, K, V, P, T, 0, h, 1 / np.sqrt(d))
+    prev = set(seeded)
+    self_evicted = kept = 0
+    for s, res in enumerate(steps):
+        t = P + s
+        cur = set(res.members)
+        assert len(cur) == h and len(cur - prev) <= 1
+        self_evicted += res.evicted == t
+        kept += t in cur
+        prev = cur
+    assert self_evicted > 0 and kept > 0
+
+
+def test_static_policy_attends_prefill_heavy_set_plus_window():
+    # Static Top-K: after a full prompt the heavy set is the prefill's and never
+    # changes; every step attends to it plus the r newest positions, which is
+    # torch's attention with that mask.
+    P, T, r, h, d = 50, 40, 6, 10, 16
+    Q, K, V = random_qkv(P + T, d, 23, spread=2.0)
+    scale = 1 / np.sqrt(d)
+    seeded, c, steps = run_trace(Q, K, V, P, T, r, h, scale, policy="static")
+    heavy0 = sorted(j for j in seeded if j < P - r)
+    assert heavy0 == sorted(prefill_keep(c, r, h))[:h]
+    N = P + T
+    mask = band_mask(N, lambda i: set(heavy0) | set(range(max(0, i - r), i + 1)))
+    ref = sdpa(Q, K, V, scale, mask=mask)
+    for s, res in enumerate(steps):
+        t = P + s
+        assert res.evicted == t - r
+        np.testing.assert_allclose(res.out, ref[t], rtol=1e-12, atol=1e-12)
+    assert sorted(steps[-1].members) == heavy0 + list(range(N - r, N))
+
+
+def test_static_policy_fills_like_h2o_before_the_cache_is_full():
+    # With a short prompt the cache fills by admission under every policy.
+    P, T, r, h, d = 4, 30, 4, 8, 8
+    Q, K, V = random_qkv(P + T, d, 24, spread=2.0)
+    _, _, st = run_trace(Q, K, V, P, T, r, h, 0.4, policy="static")
+    _, _, hh = run_trace(Q, K, V, P, T, r, h, 0.4)
+    fill = r + h - P  # steps before the first eviction
+    for s in range(fill):
+        assert st[s].evicted is None and hh[s].evicted is None
+        assert st[s].members == hh[s].members
+    assert all(res.evicted == P + s - r for s, res in enumerate(st) if s >= fill)
+
+
+def test_naive_policy_uniform_attention_is_a_sliding_window():
+    # Naive per-step Top-K with q = 0: every weight of a step is equal, ties send
+    # the older position out, so the cache is always the newest k positions:
+    # torch's attention with a band mask of width k + 1.
+    P, T, r, h, d = 30, 25, 4, 7, 8
+    k = r + h
+    rng = np.random.default_rng(25)
+    N = P + T
+    Q = np.zeros((N, d))
+    K, V = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    seeded, c, steps = run_trace(Q, K, V, P, T, r, h, 0.5, policy="naive")
+    np.testing.assert_allclose(c, np.full(P, 1.0 / P), rtol=1e-13)
+    assert sorted(seeded) == list(range(P - k, P))
+    ref = sdpa(Q, K, V, 0.5, mask=band_mask(N, lambda i: range(max(0, i - k), i + 1)))
+    for s, res in enumerate(steps):
+        t = P + s
+        assert res.evicted == t - k
+        np.testing.assert_allclose(res.out, ref[t], rtol=1e-12, atol=1e-13)
+        for j, sc in res.members.items():
+            assert sc == pytest.approx(1.0 / (k + 1), rel=1e-12)
+
+
+def test_naive_prefill_scores_are_the_last_prompt_row():
+    Q, K, _ = random_qkv(20, 8, 26, spread=2.0)
+    c = prefill_scores(Q, K, 0.35, "naive")
+    e = np.zeros(20)
+    e[-1] = 1.0
+    last = sdpa(Q, K, np.eye(20), 0.35, causal=True)[-1]
+    np.testing.assert_allclose(c, last, rtol=1e-12, atol=1e-15)
+    assert c.sum() == pytest.approx(1.0, rel=1e-13)
+
+
+def test_naive_policy_forgets_accumulated_mass():
+    # Hand-built: position 0 collected a large score in the past but gets the
+    # smallest weight now.  H2O keeps it (its accumulated score is largest);
+    # the naive policy evicts it.
+    d = 4
+    K = np.array([[5.0, 0, 0, 0], [0, 1.0, 0, 0], [0, 0, 1.0, 0], [0, 0, 0, 1.0]])
+    V = np.eye(4)
+    q = np.array([-2.0, 1.0, 0.5, 0.2])
+    members = {0: 3.0, 1: 0.2, 2: 0.1}
+    h2o = decode_step(members, 3, q, K, V, 1, 2, 1.0)
+    naive = decode_step(members, 3, q, K, V, 1, 2, 1.0, policy="naive")
+    assert naive.evicted == 0 and h2o.evicted != 0
+    w = np.exp(K @ q)
+    w /= w.sum()
+    for j in (1, 2):
+        assert naive.members[j] == pytest.approx(w[j], rel=1e-13)
