@@ -17,6 +17,7 @@ bounded sample of the same workload.
     python bench.py [--steps K] [--warmup W] [--workload opt30b] [--no-cpu-baseline]
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -79,34 +80,35 @@ def traffic_for(wl_name, waves, cache="input"):
 # ---- CPU baseline: the oracle on the host cores (runs before any GPU use) -------
 
 def _oracle_worker(args):
-    wl_name, units, steps = args
+    wl_name, recent, heavy, policy, units, steps = args
+    import dataclasses as dc
     from threadpoolctl import threadpool_limits
     from oracle import decode_step, prefill
     from synth import WORKLOADS as W, gen
-    wl = W[wl_name]
+    wl = dc.replace(W[wl_name], recent=recent, heavy=heavy)
     with threadpool_limits(1):
         data = []
         for u in units:
             b, h = divmod(u, wl.heads)
             Q, K, V = gen.unit_values(wl, b, h, 0, wl.prompt + steps)
-            m, _ = prefill(Q[:wl.prompt], K[:wl.prompt], wl.recent, wl.heavy, wl.scale)
+            m, _ = prefill(Q[:wl.prompt], K[:wl.prompt], wl.recent, wl.heavy, wl.scale, policy)
             data.append((Q, K, V, m))
         t0 = time.perf_counter()
         for Q, K, V, m in data:
             for s in range(steps):
                 t = wl.prompt + s
-                m = decode_step(m, t, Q[t], K, V, wl.recent, wl.heavy, wl.scale).members
+                m = decode_step(m, t, Q[t], K, V, wl.recent, wl.heavy, wl.scale, policy=policy).members
         dt = time.perf_counter() - t0
     return len(units) * steps, dt
 
 
-def cpu_baseline(wl, units_per_worker, steps):
+def cpu_baseline(wl, units_per_worker, steps, policy="h2o"):
     import multiprocessing as mp
     workers = min(16, len(os.sched_getaffinity(0)))
     stride = max(1, wl.units // (workers * units_per_worker))
     chosen = list(range(0, wl.units, stride))[:workers * units_per_worker]
-    jobs = [(wl.name, chosen[i::workers], steps) for i in range(workers)]
-    jobs = [j for j in jobs if j[1]]
+    jobs = [(wl.name, wl.recent, wl.heavy, policy, chosen[i::workers], steps) for i in range(workers)]
+    jobs = [j for j in jobs if j[4]]
     with mp.get_context("fork").Pool(len(jobs)) as pool:
         res = pool.map(_oracle_worker, jobs)
     unit_steps_per_s = sum(n / dt for n, dt in res)
@@ -133,7 +135,8 @@ def cpu_baseline(wl, units_per_worker, steps):
 
 # ---- GPU -----------------------------------------------------------------------
 
-def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, cache="input"):
+def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, cache="input",
+            policy="h2o"):
     import torch
     from kv_cache_eviction_02_amd import H2OCache
     from kv_cache_eviction_02_amd.binding import load_library
@@ -150,7 +153,8 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     print(f"[bench] staged inputs in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     cache = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy, wl.prompt, dtype,
-                     wl.scale, device=dev, decode_waves=waves, decode_split=split, cache=cache)
+                     wl.scale, device=dev, decode_waves=waves, decode_split=split, cache=cache,
+                     policy=policy)
     stream = torch.cuda.current_stream()
     # The first prefill also loads the kernels' code objects; the second one,
     # which rebuilds the same state from the same prompt, is the one timed.
@@ -226,6 +230,10 @@ def main():
     ap.add_argument("--decode-waves", type=int, default=0)
     ap.add_argument("--cache", default="input", choices=["input", "e4m3"],
                     help="cache rows as the input dtype, or E4M3 codes with per-row scales")
+    ap.add_argument("--policy", default="h2o", choices=["h2o", "static", "naive"],
+                    help="eviction policy: H2O or one of its ablations")
+    ap.add_argument("--heavy-only", action="store_true",
+                    help="no protected window: recent = 0, heavy = the workload's k")
     ap.add_argument("--decode-split", type=int, default=0,
                     help="decode workgroups per (batch, head) unit; 0 = library default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -243,6 +251,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     wl = WORKLOADS[args.workload]
+    if args.heavy_only:
+        wl = dataclasses.replace(wl, recent=0, heavy=wl.k)
     steps = args.steps
     warmup = args.warmup
     if warmup + steps > wl.steps:
@@ -253,19 +263,20 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
-        cpu = cpu_baseline(wl, args.cpu_units_per_worker, min(args.cpu_steps, wl.steps))
+        cpu = cpu_baseline(wl, args.cpu_units_per_worker, min(args.cpu_steps, wl.steps), args.policy)
         print(f"[bench] cpu baseline done in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     if args.cache == "e4m3" and wl.kv_dtype != "bf16":
         sys.exit("an E4M3 cache takes bf16 inputs")
     g = run_gpu(wl, steps, warmup, args.decode_waves, args.copy_calibration_mib, args.single_step_calls,
-                args.decode_split, args.cache)
+                args.decode_split, args.cache, args.policy)
     ms_per_step = g["region_ms"] / steps
     # one decode launch per step: the mean launch duration over the timed region
     mean_launch_ms = ms_per_step
     bytes_step = alg_bytes_per_step(wl, args.cache)
     achieved = bytes_step / (mean_launch_ms * 1e-3) / 1e9
-    traffic = traffic_for(wl.name, g["waves"], args.cache)
+    traffic = traffic_for(wl.name, g["waves"], args.cache) \
+        if args.policy == "h2o" and not args.heavy_only else None
     line = {
         "metric": METRIC,
         "value": 1e3 / ms_per_step,
@@ -282,7 +293,8 @@ def main():
         "config": {
             "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "head_dim": wl.head_dim,
             "prompt": wl.prompt, "k": wl.k, "recent": wl.recent, "heavy": wl.heavy,
-            "kv_dtype": wl.kv_dtype, "cache": args.cache, "decode_waves": g["waves"],
+            "kv_dtype": wl.kv_dtype, "cache": args.cache, "policy": args.policy,
+            "decode_waves": g["waves"],
             "decode_split": args.decode_split or "auto",
             "parallelism": "none",
             "launch": "h2o_decode_step per step" if args.single_step_calls else "h2o_decode_steps",

@@ -28,6 +28,8 @@
  *   slots [0, recent)  form a ring: position p lives in slot p % recent;
  *   slots [recent, k)  hold heavy hitters, filled from slot `recent` upward.
  *   An eviction overwrites at most two rows in place; nothing is moved.
+ *   With recent = 0 (no protected window) every slot is a heavy slot and the
+ *   decoded token is itself a candidate for eviction.
  *
  * Conventions
  *   - Pointers to tensors are HIP device pointers, 16-byte aligned (evicted_pos:
@@ -74,6 +76,25 @@ typedef enum { H2O_F32 = 0, H2O_BF16 = 1 } h2o_dtype;
  * decoded token's own attention use the exact bf16 rows. */
 typedef enum { H2O_CACHE_INPUT = 0, H2O_CACHE_E4M3 = 1 } h2o_cache_dtype;
 
+/* Eviction policy: H2O, or one of the ablations the pages contrast it with
+ * (summary, "Prior limits": static Top-K without heavy-hitter dynamics;
+ * "Limitations": naive Top-K each step is a different algorithm).  All three
+ * attend, admit while the cache is filling, and keep the protected window the
+ * same way.
+ *   H2O_POLICY_H2O:    scores accumulate; the victim is the lowest (score,
+ *                      position) outside the window.
+ *   H2O_POLICY_STATIC: the heavy set is chosen once by the prefill scores; once
+ *                      the cache is full the victim is always the position that
+ *                      leaves the window (t - recent), so the heavy rows never
+ *                      change and the rest is a sliding window.  Scores still
+ *                      accumulate but decide nothing.
+ *   H2O_POLICY_NAIVE:  a member's score is the weight of the current step only
+ *                      (no accumulation); the prefill ranks prompt positions by
+ *                      the attention of the last prompt token; the victim is the
+ *                      lowest (score, position) outside the window.
+ * The heavy-only ablation is recent = 0 under H2O_POLICY_H2O. */
+typedef enum { H2O_POLICY_H2O = 0, H2O_POLICY_STATIC = 1, H2O_POLICY_NAIVE = 2 } h2o_policy;
+
 /* Largest budget k = recent + heavy the decode kernel accepts (its per-row
  * logits live in LDS). */
 #define H2O_MAX_K 8192
@@ -82,8 +103,8 @@ typedef struct {
   int32_t batch;       /* >= 1 */
   int32_t heads;       /* >= 1 */
   int32_t head_dim;    /* 64, 96 or 128 */
-  int32_t recent;      /* r >= 1: size of the protected window (includes the decoded token) */
-  int32_t heavy;       /* h >= 0: heavy-hitter slots; k = r + h <= H2O_MAX_K */
+  int32_t recent;      /* r >= 0: size of the protected window (includes the decoded token) */
+  int32_t heavy;       /* h >= 0: heavy-hitter slots; 1 <= k = r + h <= H2O_MAX_K */
   int32_t max_prompt;  /* >= 0: longest prompt h2o_prefill will accept (sizes the scratch) */
   int32_t kv_dtype;    /* h2o_dtype of q, k, v inputs and of the K/V slots */
   float scale;         /* softmax scale; 0 selects 1/sqrt(head_dim) */
@@ -94,6 +115,7 @@ typedef struct {
                           2..64 = that many (each streams a share of the rows; for batches
                           with few units) */
   int32_t cache_dtype; /* h2o_cache_dtype */
+  int32_t policy;      /* h2o_policy */
 } h2o_config;
 
 typedef struct {

@@ -14,6 +14,8 @@ LIB_PATH = os.path.join(PKG, "libh2o.so")
 H2O_OK, H2O_ERR_INVALID, H2O_ERR_UNSUPPORTED, H2O_ERR_STATE, H2O_ERR_OOM, H2O_ERR_HIP = range(6)
 H2O_F32, H2O_BF16 = 0, 1
 H2O_CACHE_INPUT, H2O_CACHE_E4M3 = 0, 1
+H2O_POLICY_H2O, H2O_POLICY_STATIC, H2O_POLICY_NAIVE = 0, 1, 2
+POLICIES = {"h2o": H2O_POLICY_H2O, "static": H2O_POLICY_STATIC, "naive": H2O_POLICY_NAIVE}
 H2O_MAX_K = 8192
 
 STATUS_NAMES = {
@@ -41,6 +43,7 @@ class h2o_config(ctypes.Structure):
         ("decode_waves", ctypes.c_int32),
         ("decode_split", ctypes.c_int32),
         ("cache_dtype", ctypes.c_int32),
+        ("policy", ctypes.c_int32),
     ]
 
 
@@ -150,7 +153,7 @@ class H2OCache:
 
     def __init__(self, batch, heads, head_dim, recent, heavy, max_prompt, dtype,
                  scale=0.0, device="cuda", decode_waves=0, start_pos=0, start_live=0,
-                 state=None, decode_split=0, cache="input"):
+                 state=None, decode_split=0, cache="input", policy="h2o"):
         import torch
         self.torch = torch
         load_library()
@@ -158,6 +161,9 @@ class H2OCache:
             raise ValueError("dtype must be torch.float32 or torch.bfloat16")
         if cache not in ("input", "e4m3"):
             raise ValueError("cache must be 'input' or 'e4m3'")
+        if policy not in POLICIES:
+            raise ValueError(f"policy must be one of {sorted(POLICIES)}")
+        self.policy = policy
         self.batch, self.heads, self.head_dim = batch, heads, head_dim
         self.recent, self.heavy, self.k = recent, heavy, recent + heavy
         self.dtype = dtype
@@ -179,17 +185,20 @@ class H2OCache:
         else:
             self.k_slots, self.v_slots, self.score, self.pos = state[:4]
             self.k_scale, self.v_scale = (state[4], state[5]) if len(state) > 4 else (None, None)
-        checks = [(self.k_slots, slot_dtype), (self.v_slots, slot_dtype),
-                  (self.score, torch.float32), (self.pos, torch.int32)]
+        checks = [(self.k_slots, slot_dtype, shape), (self.v_slots, slot_dtype, shape),
+                  (self.score, torch.float32, shape[:3]), (self.pos, torch.int32, shape[:3])]
         if cache == "e4m3":
-            checks += [(self.k_scale, torch.float32), (self.v_scale, torch.float32)]
-        for t_, dt in checks:
-            if t_ is None or t_.dtype != dt or not t_.is_contiguous() or t_.device != self.device:
-                raise ValueError("state tensors must be contiguous, on the device, with the right dtypes")
+            checks += [(self.k_scale, torch.float32, shape[:3]), (self.v_scale, torch.float32, shape[:3])]
+        for t_, dt, shp in checks:
+            if t_ is None or t_.dtype != dt or tuple(t_.shape) != shp or not t_.is_contiguous() \
+                    or t_.device != self.device:
+                raise ValueError("state tensors must be contiguous, on the device, with the "
+                                 "layout's shapes and dtypes")
         self.cfg = h2o_config(batch, heads, head_dim, recent, heavy, max_prompt,
                               H2O_F32 if dtype == torch.float32 else H2O_BF16, scale,
                               start_pos, start_live, decode_waves, decode_split,
-                              H2O_CACHE_E4M3 if cache == "e4m3" else H2O_CACHE_INPUT)
+                              H2O_CACHE_E4M3 if cache == "e4m3" else H2O_CACHE_INPUT,
+                              POLICIES[policy])
         self.state = h2o_state(self.k_slots.data_ptr(), self.v_slots.data_ptr(),
                                self.score.data_ptr(), self.pos.data_ptr(),
                                self.k_scale.data_ptr() if self.k_scale is not None else None,

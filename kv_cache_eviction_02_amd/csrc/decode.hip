@@ -10,6 +10,10 @@
 //   when the cache was full (k live slots), evict the slot with the smallest
 //   (score, position) among the heavy slots and the ring slot whose position
 //   t - r just left the protected window.
+// Ablations of the same step (summary, "Prior limits" and "Limitations"): the
+// static policy always evicts the position leaving the window, the naive one
+// replaces each score by the current weight instead of adding it, and r = 0
+// (heavy-only) makes the decoded token itself a candidate.
 //
 // Two kernels share the streaming loop and the final score/eviction code:
 //
@@ -80,14 +84,22 @@ struct Geo {
   static_assert(!kQuant || std::is_same<T, bf16>::value, "E4M3 cache takes bf16 inputs");
 };
 
-// One unit's step as seen by every thread.
+constexpr int kSelfVictim = -2;  // victim marker: the decoded token itself (r = 0)
+
+// One unit's step as seen by every thread.  With r = 0 there is no ring:
+// ring_slot is -1 and every slot is a heavy slot.
 struct StepView {
-  int k, r, t, n_ring, n_heavy, n_live, n_att, ring_slot;
+  int k, r, t, n_ring, n_heavy, n_live, n_att, ring_slot, policy;
   bool full, ring_live;
   __device__ StepView(const DecodeArgs& a)
       : k(a.k), r(a.r), t(a.t), n_ring(a.n_ring), n_heavy(a.n_heavy),
-        n_live(a.n_ring + a.n_heavy), n_att(a.n_ring + a.n_heavy + 1), ring_slot(a.t % a.r),
-        full(a.n_ring + a.n_heavy == a.k), ring_live(a.t % a.r < a.n_ring) {}
+        n_live(a.n_ring + a.n_heavy), n_att(a.n_ring + a.n_heavy + 1),
+        ring_slot(a.r > 0 ? a.t % a.r : -1), policy(a.policy), full(a.n_ring + a.n_heavy == a.k),
+        ring_live(a.r > 0 && a.t % a.r < a.n_ring) {}
+  // Victim when the argmin does not run (static policy): the newest candidate,
+  // i.e. the position leaving the window, or the decoded token when r = 0.
+  __device__ int fixed_victim() const { return r > 0 ? ring_slot : kSelfVictim; }
+  __device__ int fixed_victim_pos() const { return t - r; }
   // Logical row j: live ring slots [0, n_ring), then live heavy slots; row n_live is the new token.
   __device__ int slot_of(int j) const { return j < n_ring ? j : r + (j - n_ring); }
   __device__ bool is_cand(int s) const { return full && (s >= r || s == ring_slot); }
@@ -324,10 +336,10 @@ __device__ __forceinline__ GroupMerge<GG::NG> merge_groups(float m, float lsum, 
   return r;
 }
 
-// Quantize the decoded token's K and V rows into the ring slot (E4M3 cache):
+// Quantize the decoded token's K and V rows into slot `slot` (E4M3 cache):
 // lanes [0, G) of wave 0 take K, lanes [G, 2G) take V, each lane 16 values.
 template <typename GG>
-__device__ inline void admit_quantized(const StepView& v, const UnitPtrs<GG>& u) {
+__device__ inline void admit_quantized(const UnitPtrs<GG>& u, int slot) {
   constexpr int G = GG::G, LPR = GG::LPR, EPL = GG::EPL;
   const int tid = threadIdx.x;
   if (tid >= 2 * G) return;
@@ -340,9 +352,9 @@ __device__ inline void admit_quantized(const StepView& v, const UnitPtrs<GG>& u)
 #pragma unroll
   for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
   amax = group_max<G>(act ? amax : 0.f);
-  char* row = (is_v ? u.V : u.K) + (size_t)v.ring_slot * GG::ROWB;
+  char* row = (is_v ? u.V : u.K) + (size_t)slot * GG::ROWB;
   if (act) store16(row + c * 16, quantize16_e4m3(x, amax));
-  if (c == 0) (is_v ? u.vs : u.ks)[v.ring_slot] = __fdiv_rn(amax, 448.f);
+  if (c == 0) (is_v ? u.vs : u.ks)[slot] = __fdiv_rn(amax, 448.f);
 }
 
 // Score update, eviction argmin and admission for one unit, given the exact
@@ -361,12 +373,18 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const float p_self = fast_exp2(s_logit[v.n_live] - M) * invL;
+  const bool naive = v.policy == 2;      // score = this step's weight
+  const bool argmin = v.policy != 1;     // static: fixed victim
 
   unsigned long long best = ~0ull;
   int best_slot = -1;
+  if (v.r == 0 && tid == 0) {  // no window: the decoded token competes too
+    best = ((unsigned long long)__float_as_uint(p_self) << 32) | (uint32_t)v.t;
+    best_slot = kSelfVictim;
+  }
   auto update = [&](int j, float old, int ps) {
     const int s = v.slot_of(j);
-    const float ns = old + fast_exp2(s_logit[j] - M) * invL;
+    const float ns = (naive ? 0.f : old) + fast_exp2(s_logit[j] - M) * invL;
     s_logit[j] = ns;
     if (v.is_cand(s)) {
       const unsigned long long key = ((unsigned long long)__float_as_uint(ns) << 32) | (uint32_t)ps;
@@ -387,7 +405,9 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
   }
 
   unsigned long long vkey = ~0ull;
-  if (v.full) {
+  if (v.full && !argmin) {
+    vkey = (uint32_t)v.fixed_victim_pos();  // s_victim keeps its initial fixed_victim()
+  } else if (v.full) {
     unsigned long long w = best;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -398,23 +418,29 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < NW; ++i) vkey = s_key[i] < vkey ? s_key[i] : vkey;
-    if (best_slot >= 0 && best == vkey) *s_victim = best_slot;
+    if (best_slot != -1 && best == vkey) *s_victim = best_slot;
   }
   __syncthreads();
 
-  // Where the row leaving the window goes: the victim's heavy slot, or the next
-  // free heavy slot while the cache is not yet full; -1 if it is dropped or
-  // still inside the window.
-  int dst = -1;
-  if (v.full) {
-    if (*s_victim != v.ring_slot) dst = *s_victim;
-  } else if (v.ring_live) {
-    dst = v.r + v.n_heavy;
+  // dst: where the row leaving the window goes (the victim's heavy slot, or the
+  // next free heavy slot while the cache is not yet full; -1 if it is dropped or
+  // still inside the window).  adm: where the decoded token goes (its ring slot;
+  // with r = 0 the victim's slot or the next free one, -1 if it is the victim).
+  int dst = -1, adm;
+  if (v.r > 0) {
+    adm = v.ring_slot;
+    if (v.full) {
+      if (*s_victim != v.ring_slot) dst = *s_victim;
+    } else if (v.ring_live) {
+      dst = v.r + v.n_heavy;
+    }
+  } else {
+    adm = v.full ? (*s_victim == kSelfVictim ? -1 : *s_victim) : v.n_live;
   }
 
   auto write_score = [&](int j) {
     const int s = v.slot_of(j);
-    if (s != v.ring_slot && s != dst) u.score[s] = s_logit[j];
+    if (s != adm && s != dst) u.score[s] = s_logit[j];
   };
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
@@ -432,19 +458,23 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
         u.vs[dst] = st->ring_scale[1];
       }
     }
-    u.score[v.ring_slot] = p_self;
-    u.pos[v.ring_slot] = v.t;
+    if (adm >= 0) {
+      u.score[adm] = p_self;
+      u.pos[adm] = v.t;
+    }
     if (evicted) evicted[unit] = v.full ? (int32_t)(uint32_t)vkey : -1;
   }
   if (tid < LPR && dst >= 0) {
     store16(u.K + (size_t)dst * ROWB + tid * 16, st->ring[0][tid]);
     store16(u.V + (size_t)dst * ROWB + tid * 16, st->ring[1][tid]);
   }
-  if constexpr (GG::kQuant) {
-    admit_quantized<GG>(v, u);
-  } else if (tid < LPR) {
-    store16(u.K + (size_t)v.ring_slot * ROWB + tid * 16, st->self[0][tid]);
-    store16(u.V + (size_t)v.ring_slot * ROWB + tid * 16, st->self[1][tid]);
+  if (adm >= 0) {
+    if constexpr (GG::kQuant) {
+      admit_quantized<GG>(u, adm);
+    } else if (tid < LPR) {
+      store16(u.K + (size_t)adm * ROWB + tid * 16, st->self[0][tid]);
+      store16(u.V + (size_t)adm * ROWB + tid * 16, st->self[1][tid]);
+    }
   }
 }
 
@@ -485,7 +515,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int gl = (tid & 63) & (GG::G - 1);
   const bool act = gl < LPR;
 
-  if (tid == 0) s_victim = v.ring_slot;  // overwritten by the argmin owner when the cache is full
+  if (tid == 0) s_victim = v.fixed_victim();  // overwritten by the argmin owner when the cache is full
 
   float qf[EPL];
   load_input<GG>(u.q, act ? gl : 0, qf);
@@ -538,7 +568,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   const int gl = (tid & 63) & (GG::G - 1);
   const bool act = gl < LPR;
 
-  if (tid == 0) s_victim = v.ring_slot;
+  if (tid == 0) s_victim = v.fixed_victim();
 
   float qf[EPL];
   load_input<GG>(u.q, act ? gl : 0, qf);

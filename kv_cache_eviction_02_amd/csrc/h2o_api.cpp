@@ -32,7 +32,9 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
 bool valid_dims(const h2o_config* c) {
-  return c->batch >= 1 && c->heads >= 1 && c->recent >= 1 && c->heavy >= 0 &&
+  return c->batch >= 1 && c->heads >= 1 && c->recent >= 0 && c->heavy >= 0 &&
+         (int64_t)c->recent + c->heavy >= 1 &&
+         (c->policy == H2O_POLICY_H2O || c->policy == H2O_POLICY_STATIC || c->policy == H2O_POLICY_NAIVE) &&
          c->max_prompt >= 0 && (c->kv_dtype == H2O_F32 || c->kv_dtype == H2O_BF16) &&
          isfinite(c->scale) && c->scale >= 0.f && c->start_pos >= 0 && c->start_live >= 0 &&
          (c->decode_waves == 0 || c->decode_waves == 1 || c->decode_waves == 2 ||
@@ -157,6 +159,7 @@ h2o_status h2o_prefill_with_output(h2o_ctx* ctx, const void* q, const void* k, c
   a.r = ctx->cfg.recent;
   a.h = ctx->cfg.heavy;
   a.scale_log2 = ctx->scale_log2;
+  a.last_row_only = ctx->cfg.policy == H2O_POLICY_NAIVE;
   const hipError_t e = h2o::launch_prefill(a, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype,
                                            ctx->cfg.head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return from_hip(e);
@@ -194,6 +197,7 @@ h2o_status enqueue_step(h2o_ctx* ctx, const void* q, const void* k_new, const vo
   a.n_ring = n_ring;
   a.n_heavy = ctx->n_live - n_ring;
   a.scale_log2 = ctx->scale_log2;
+  a.policy = ctx->cfg.policy;
   const hipError_t e = h2o::launch_decode(a, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype,
                                           ctx->cfg.head_dim, ctx->waves, &ctx->split, stream);
   if (e != hipSuccess) return from_hip(e);

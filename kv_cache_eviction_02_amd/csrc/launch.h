@@ -24,6 +24,7 @@ struct DecodeArgs {
   int32_t n_ring;      // live ring slots: min(t, r)
   int32_t n_heavy;     // live heavy slots
   float scale_log2;    // softmax scale * log2(e)
+  int32_t policy;      // 0 H2O, 1 static (victim = position leaving the window), 2 naive (no accumulation)
 };
 
 // Scratch of the split decode (several workgroups per unit).
@@ -52,6 +53,7 @@ struct PrefillArgs {
   int32_t P;
   int32_t k, r, h;
   float scale_log2;
+  int32_t last_row_only;  // scores = attention of the last prompt row (naive policy), not column sums
 };
 
 // dtype: 0 = float32, 1 = bfloat16 (inputs); cache: 0 = slots in the input

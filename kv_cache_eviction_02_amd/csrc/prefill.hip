@@ -439,7 +439,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 
 // Column sums c_j = sum_{i >= j} exp2(s_ij - lse_i).  A wavefront owns
 // kFixed*16 keys and walks the query subtiles from its first key to the end
-// of the prompt in a fixed order, so the sums are deterministic.
+// of the prompt in a fixed order, so the sums are deterministic.  With
+// last_row_only (naive per-step Top-K) only the last prompt row contributes:
+// c_j = exp2(s_{P-1,j} - lse_{P-1}).
 template <typename T, int D>
 __global__ __launch_bounds__(kWaves * 64) void colsum_kernel(PrefillArgs a, int stride, int nblk) {
   constexpr int QS = kFixed<T>;
@@ -464,13 +466,16 @@ __global__ __launch_bounds__(kWaves * 64) void colsum_kernel(PrefillArgs a, int 
   float cs[QS];
 #pragma unroll
   for (int q = 0; q < QS; ++q) cs[q] = 0.f;
-  const int qt0 = j0 / kTile;
   const int nqt = (P + kTile - 1) / kTile;
+  const bool last_only = a.last_row_only != 0;
+  const int qt0 = last_only ? nqt - 1 : j0 / kTile;  // j0 <= P - 1, so j0 / kTile <= nqt - 1
+  const int q_lo = last_only ? P - 1 : 0;          // first query row that counts
 
   auto step = [&](int qt, const Frag<T, D>& fq, const float4& lq) {
     const int i0 = qt * kTile;
     const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
-    const bool edge = i0 < j0 + ROWS - 1 || i0 + kTile > P;  // uniform: masking needed
+    // uniform: masking needed
+    const bool edge = last_only || i0 < j0 + ROWS - 1 || i0 + kTile > P;
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
       const f32x4 acc = tile_dot<T, D>(fq, fk[q]);
@@ -480,7 +485,7 @@ __global__ __launch_bounds__(kWaves * 64) void colsum_kernel(PrefillArgs a, int 
       for (int i = 0; i < 4; ++i) {
         const float p = fast_exp2(fmaf(acc[i], a.scale_log2, -lv[i]));
         const int qi = i0 + g4 + i;
-        add += (!edge || (qi >= kj && qi < P)) ? p : 0.f;
+        add += (!edge || (qi >= kj && qi < P && qi >= q_lo)) ? p : 0.f;
       }
       cs[q] += add;
     }

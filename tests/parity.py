@@ -78,19 +78,20 @@ class Harness:
     """Runs one workload on the GPU and checks sampled units against the oracle."""
 
     def __init__(self, wl, units, steps, device="cuda", decode_waves=0, decode_split=0,
-                 cache="input"):
+                 cache="input", policy="h2o"):
         self.wl = wl
         self.units = units
         self.steps = steps
         self.device = device
         self.stats = Stats()
         self.cache_kind = cache
+        self.policy = policy
         U, k = wl.units, wl.k
         self.idx = torch.tensor(units, dtype=torch.long, device=device)
         self.cache = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy,
                               max_prompt=wl.prompt, dtype=torch_dtype(wl), scale=wl.scale,
                               device=device, decode_waves=decode_waves, decode_split=decode_split,
-                              cache=cache)
+                              cache=cache, policy=policy)
         self.flat = dict(pos=self.cache.pos.view(U, k), score=self.cache.score.view(U, k),
                          k=self.cache.k_slots.view(U, k, -1), v=self.cache.v_slots.view(U, k, -1))
         if cache == "e4m3":
@@ -154,7 +155,7 @@ class Harness:
         pos, score = self.gather("pos"), self.gather("score")
         for i, u in enumerate(self.units):
             Q, K, _ = self.vals[u]
-            ref, c = prefill(Q[:P], K[:P], r, h, wl.scale)
+            ref, c = prefill(Q[:P], K[:P], r, h, wl.scale, self.policy)
             got = members_from_slots(pos[i], score[i])
             n_ring = min(P, r)
             # ring slots hold the newest positions at slot = position % r
@@ -236,7 +237,7 @@ class Harness:
             Q, K, V = self.vals[u]
             members = members_from_slots(before[0][i], before[1][i])
             Kc, Vc = self.cached.get(u, (None, None))
-            res = decode_step(members, t, Q[t], K, V, r, h, wl.scale, Kc, Vc)
+            res = decode_step(members, t, Q[t], K, V, r, h, wl.scale, Kc, Vc, self.policy)
             scale_o = np.abs(res.out).max()
             err_o = np.abs(out[i] - res.out).max()
             assert err_o <= 2e-3 * scale_o, (u, t, err_o, scale_o)
@@ -247,7 +248,10 @@ class Harness:
             if res.evicted is None:
                 assert got_ev == -1, (u, t, got_ev)
             elif got_ev != res.evicted:
-                pre = {j: members[j] + res.weights[j] for j in members}
+                # the static victim is fixed by positions alone: no tolerance
+                assert self.policy != "static", (u, t, got_ev, res.evicted)
+                keep = 0.0 if self.policy == "naive" else 1.0
+                pre = {j: keep * members[j] + res.weights[j] for j in members}
                 pre[t] = res.weights[t]
                 cands = sorted((sc, j) for j, sc in pre.items() if j <= t - r)
                 lo = cands[0][0]

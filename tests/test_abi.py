@@ -25,7 +25,7 @@ def header_functions():
 def cfg(**kw):
     base = dict(batch=2, heads=3, head_dim=64, recent=4, heavy=4, max_prompt=0,
                 kv_dtype=B.H2O_BF16, scale=0.0, start_pos=0, start_live=0, decode_waves=0,
-                decode_split=0, cache_dtype=0)
+                decode_split=0, cache_dtype=0, policy=0)
     base.update(kw)
     return B.h2o_config(**base)
 
@@ -55,10 +55,11 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stdio.h>
 #include "h2o.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(h2o_config), offsetof(h2o_config, scale),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(h2o_config), offsetof(h2o_config, scale),
          offsetof(h2o_config, decode_waves), sizeof(h2o_state), offsetof(h2o_state, pos),
          offsetof(h2o_config, decode_split), offsetof(h2o_config, cache_dtype),
-         offsetof(h2o_state, v_scale));
+         offsetof(h2o_state, v_scale), offsetof(h2o_config, policy));
+  printf("%d %d %d\n", H2O_POLICY_H2O, H2O_POLICY_STATIC, H2O_POLICY_NAIVE);
   printf("%d\n", H2O_MAX_K);
   return 0;
 }''')
@@ -69,8 +70,11 @@ int main(void) {
     assert got == [ctypes.sizeof(B.h2o_config), B.h2o_config.scale.offset,
                    B.h2o_config.decode_waves.offset, ctypes.sizeof(B.h2o_state),
                    B.h2o_state.pos.offset, B.h2o_config.decode_split.offset,
-                   B.h2o_config.cache_dtype.offset, B.h2o_state.v_scale.offset]
-    assert int(lines[1]) == B.H2O_MAX_K
+                   B.h2o_config.cache_dtype.offset, B.h2o_state.v_scale.offset,
+                   B.h2o_config.policy.offset]
+    assert list(map(int, lines[1].split())) == [B.H2O_POLICY_H2O, B.H2O_POLICY_STATIC,
+                                                B.H2O_POLICY_NAIVE]
+    assert int(lines[2]) == B.H2O_MAX_K
 
 
 def test_status_strings():
@@ -82,7 +86,10 @@ def test_status_strings():
 @pytest.mark.parametrize("kw,expect", [
     (dict(batch=0), B.H2O_ERR_INVALID),
     (dict(heads=-1), B.H2O_ERR_INVALID),
-    (dict(recent=0), B.H2O_ERR_INVALID),
+    (dict(recent=-1), B.H2O_ERR_INVALID),
+    (dict(recent=0, heavy=0), B.H2O_ERR_INVALID),                   # empty budget
+    (dict(policy=3), B.H2O_ERR_INVALID),
+    (dict(policy=-1), B.H2O_ERR_INVALID),
     (dict(heavy=-1), B.H2O_ERR_INVALID),
     (dict(max_prompt=-5), B.H2O_ERR_INVALID),
     (dict(kv_dtype=7), B.H2O_ERR_INVALID),
@@ -187,3 +194,13 @@ def test_e4m3_cache_needs_aligned_scales():
     assert st == B.H2O_OK
     k2.h2o_destroy(ctx)
     assert k2.h2o_create(cfg(cache_dtype=1), state(ks=FAKE + 4, vs=FAKE))[0] == B.H2O_ERR_INVALID
+
+
+@pytest.mark.parametrize("policy", [0, 1, 2])
+def test_create_accepts_policies_and_heavy_only(policy):
+    for kw in (dict(policy=policy), dict(policy=policy, recent=0, heavy=8),
+               dict(policy=policy, recent=0, heavy=8, start_pos=20, start_live=8)):
+        st, ctx = k2.h2o_create(cfg(**kw), state())
+        assert st == B.H2O_OK and ctx
+        assert k2.h2o_query(ctx) == (B.H2O_OK, kw.get("start_pos", 0), kw.get("start_live", 0))
+        assert k2.h2o_destroy(ctx) == B.H2O_OK

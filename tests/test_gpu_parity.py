@@ -35,13 +35,15 @@ def _need_gpu():
 
 
 def run_workload(wl, n_units, steps, check_every=1, decode_waves=0, kv_every=64, decode_split=0,
-                 cache="input", prompt_output=False):
+                 cache="input", prompt_output=False, policy="h2o"):
     from parity import Harness, sample_units
     units = sample_units(wl, n_units)
     say(f"[parity] {wl.name} B={wl.batch} H={wl.heads} d={wl.head_dim} P={wl.prompt} "
         f"k={wl.k} ({wl.recent}+{wl.heavy}) {wl.kv_dtype} steps={steps} units={units[:6]}... "
-        f"waves={decode_waves} split={decode_split} cache={cache} prompt_output={prompt_output}")
-    hn = Harness(wl, units, steps, decode_waves=decode_waves, decode_split=decode_split, cache=cache)
+        f"waves={decode_waves} split={decode_split} cache={cache} prompt_output={prompt_output} "
+        f"policy={policy}")
+    hn = Harness(wl, units, steps, decode_waves=decode_waves, decode_split=decode_split, cache=cache,
+                 policy=policy)
     try:
         hn.prefill(output=prompt_output)
         stats = hn.run(check_every=check_every, kv_every=kv_every)
@@ -341,3 +343,43 @@ def test_prompt_output_large_prompt_and_e4m3_cache():
                   zipf_alpha=1.1)
     run_workload(wl, 2, 8, kv_every=4, prompt_output=True)
     run_workload(wl, 2, 8, kv_every=4, prompt_output=True, cache="e4m3")
+
+
+# ---- ablation policies: static Top-K, naive per-step Top-K, heavy-only (r = 0) ----------
+
+def heavy_only(wl, cid):
+    """The workload's budget k with no protected window."""
+    import dataclasses
+    return dataclasses.replace(wl, cid=cid, name=wl.name + "_heavy_only", recent=0, heavy=wl.k)
+
+
+@pytest.mark.parametrize("policy", ["static", "naive"])
+@pytest.mark.parametrize("name,units,steps", [("tiny_fp32", 2, 64), ("opt6.7b", 8, 96), ("opt30b", 4, 24),
+                                              ("llama7b_stream", 4, 300)])
+def test_policy_workloads(policy, name, units, steps):
+    run_workload(WORKLOADS[name], units, steps, kv_every=8, policy=policy)
+
+
+@pytest.mark.parametrize("policy", ["h2o", "naive", "static"])
+@pytest.mark.parametrize("name,units,steps", [("tiny_fp32", 2, 64), ("opt6.7b", 8, 96),
+                                              ("llama7b_stream", 4, 300)])
+def test_heavy_only_workloads(policy, name, units, steps):
+    wl = heavy_only(WORKLOADS[name], 200 + list(WORKLOADS).index(name))
+    stats = run_workload(wl, units, steps, kv_every=8, policy=policy)
+    assert stats.steps == steps
+
+
+@pytest.mark.parametrize("split", [1, 4])
+@pytest.mark.parametrize("policy", ["h2o", "static", "naive"])
+@pytest.mark.parametrize("wl", EDGE, ids=lambda w: w.name)
+def test_policy_edge_cases(wl, policy, split):
+    run_workload(wl, wl.units, wl.steps, kv_every=1, decode_split=split, policy=policy)
+    run_workload(heavy_only(wl, wl.cid + 100), wl.units, wl.steps, kv_every=1, decode_split=split,
+                 policy=policy)
+
+
+@pytest.mark.parametrize("policy", ["static", "naive"])
+def test_policy_e4m3_cache_and_prompt_output(policy):
+    wl = WORKLOADS["opt6.7b"]
+    run_workload(wl, 6, 64, kv_every=8, cache="e4m3", prompt_output=True, policy=policy)
+    run_workload(heavy_only(wl, 250), 6, 64, kv_every=8, cache="e4m3", policy=policy)
