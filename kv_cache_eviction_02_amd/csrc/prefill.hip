@@ -62,6 +62,16 @@ struct Frag {
       for (int i = 0; i < kChunks; ++i) c[i] = make_uint4(0, 0, 0, 0);
     }
   }
+
+  // Row min(row0 + lane % 16, n - 1): an unconditional load (the compiler then
+  // counts outstanding loads exactly); rows past n hold a copy of row n - 1 and
+  // must be masked by the caller.
+  __device__ inline void load_clamped(const char* base, int row0, int n, int lane) {
+    const int row = min(row0 + (lane & 15), n - 1);
+    const char* p = base + (size_t)row * (D * Elem<T>::kBytes) + (lane >> 4) * kBytes;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) c[i] = load16(p + 16 * i);
+  }
 };
 
 // acc[i] = dot(moving row 4*(lane/16)+i, fixed row lane%16)
@@ -104,101 +114,6 @@ constexpr int kFixed = sizeof(T) == 2 ? 4 : 2;
 template <typename T>
 constexpr int rows_per_wave() { return kFixed<T> * kTile; }
 
-// Row statistics: lse_i = m_i + log2(sum_{j <= i} exp2(s_ij - m_i)), with
-// s = scale*log2(e) * q_i . k_j.  A wavefront owns kFixed*16 queries and walks
-// the key subtiles up to its last query, the next subtile in flight while the
-// current one is multiplied; the running max is rescaled once per pair of
-// subtiles, and the scale is folded into the exp2 argument.
-template <typename T, int D>
-__global__ __launch_bounds__(kWaves * 64) void rowstats_kernel(PrefillArgs a, int stride, int nblk) {
-  constexpr int QS = kFixed<T>;
-  constexpr int ROWS = rows_per_wave<T>();
-  constexpr float kLow = -1.0e30f;  // finite start for the running max: no inf - inf
-  const int id = xcd_local_block(nblk * a.units);
-  const int unit = id / nblk;
-  const int blk = nblk - 1 - id % nblk;  // longest rows first
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int P = a.P;
-  const int i0 = (blk * kWaves + wave) * ROWS;
-  if (i0 >= P) return;
-  constexpr int ROWB = D * Elem<T>::kBytes;
-  const char* Qb = (const char*)a.pq + (size_t)unit * P * ROWB;
-  const char* Kb = (const char*)a.pk + (size_t)unit * P * ROWB;
-  const float sc = a.scale_log2;
-
-  Frag<T, D> fq[QS];
-#pragma unroll
-  for (int q = 0; q < QS; ++q) fq[q].load(Qb, i0 + q * kTile, P, lane);
-  const int g4 = (lane >> 4) * 4;
-  float m[QS], l[QS];
-#pragma unroll
-  for (int q = 0; q < QS; ++q) {
-    m[q] = kLow;
-    l[q] = 0.f;
-  }
-  const int kend = min(P, i0 + ROWS);  // keys past the wave's last query are masked anyway
-  const int nkt = (kend + kTile - 1) / kTile;
-
-  // Raw products of one key subtile against every fixed subtile, masked to
-  // -inf where the key follows the query or does not exist.
-  auto mult = [&](int kt, const Frag<T, D>& fk, f32x4 (&acc)[QS]) {
-    const int j0 = kt * kTile;
-    const bool diag = j0 + kTile - 1 > i0;  // uniform
-#pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      acc[q] = tile_dot<T, D>(fk, fq[q]);
-      if (diag || kt >= nkt) {
-        const int qi = i0 + q * kTile + (lane & 15);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[q][i] = (kt < nkt && j0 + g4 + i <= qi) ? acc[q][i] : -INFINITY;
-      }
-    }
-  };
-  auto update = [&](const f32x4 (&x)[QS], const f32x4 (&y)[QS]) {
-#pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      float mx = fmaxf(fmaxf(x[q][0], x[q][1]), fmaxf(x[q][2], x[q][3]));
-      mx = fmaxf(mx, fmaxf(fmaxf(y[q][0], y[q][1]), fmaxf(y[q][2], y[q][3])));
-      const float mn = fmaxf(m[q], mx * sc);
-      float add = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        add += fast_exp2(fmaf(x[q][i], sc, -mn));
-        add += fast_exp2(fmaf(y[q][i], sc, -mn));
-      }
-      l[q] = fmaf(l[q], fast_exp2(m[q] - mn), add);
-      m[q] = mn;
-    }
-  };
-
-  Frag<T, D> fa, fb;
-  f32x4 ax[QS], ay[QS];
-  fa.load(Kb, 0, P, lane);
-  for (int kt = 0; kt < nkt; kt += 2) {
-    fb.load(Kb, (kt + 1) * kTile, P, lane);  // zero rows past the prompt
-    mult(kt, fa, ax);
-    if (kt + 2 < nkt) fa.load(Kb, (kt + 2) * kTile, P, lane);
-    mult(kt + 1, fb, ay);
-    update(ax, ay);
-  }
-  // Merge the four lane groups holding the same queries.
-#pragma unroll
-  for (int q = 0; q < QS; ++q) {
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      const float mo = __shfl_xor(m[q], off, 64);
-      const float lo = __shfl_xor(l[q], off, 64);
-      const float mn = fmaxf(m[q], mo);
-      l[q] = l[q] * fast_exp2(m[q] - mn) + lo * fast_exp2(mo - mn);
-      m[q] = mn;
-    }
-    const int qi = i0 + q * kTile + lane;
-    if (lane < 16 && qi < P) a.row_lse[(size_t)unit * stride + qi] = m[q] + __log2f(l[q]);
-  }
-}
-
 // ---- prompt attention output --------------------------------------------------
 //
 // O_i = sum_{j <= i} softmax_i(s_ij) v_j for every prompt row (the full causal
@@ -219,9 +134,10 @@ __global__ __launch_bounds__(kWaves * 64) void rowstats_kernel(PrefillArgs a, in
 // probabilities of a chunk enter one MFMA.  The maximum is raised only when a
 // chunk exceeds it by more than kLazy (log2 units): unnormalised probabilities
 // stay below 2^kLazy and most chunks need no rescale of the accumulators.
-template <typename T, int D>
+template <typename T, int D, bool OUT>
 struct AttendTile {
-  static constexpr int QS = 2;                        // fixed query subtiles per wavefront
+  // fixed query subtiles per wavefront: the output accumulators limit it to 2
+  static constexpr int QS = OUT || sizeof(T) == 4 ? 2 : 4;
   static constexpr int ROWS = QS * kTile;             // queries per wavefront
   static constexpr int BQ = kWaves * ROWS;            // queries per block
   static constexpr int KC = 2 * kTile;                // keys per chunk
@@ -231,11 +147,16 @@ struct AttendTile {
   static constexpr int PIECES = KC * ROWB / 16;       // 16-byte pieces of a K (or V) chunk
   static constexpr int PER_T = (PIECES + kWaves * 64 - 1) / (kWaves * 64);
   static constexpr int NDT = D / 16;                  // 16-wide output column tiles
-  static constexpr int BUF = KC * (KSTR + VSTR);      // bytes of one K + V chunk
+  static constexpr int BUF = KC * (KSTR + (OUT ? VSTR : 0));  // bytes of one K (+ V) chunk
   static constexpr int NBUF = 2 * BUF <= 60 * 1024 ? 2 : 1;
 };
 
 constexpr float kLazy = 8.f;
+
+// x, or zeros when !keep (a value select: no branch, no address select).
+__device__ inline uint4 zero_unless(bool keep, uint4 x) {
+  return make_uint4(keep ? x.x : 0u, keep ? x.y : 0u, keep ? x.z : 0u, keep ? x.w : 0u);
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -248,10 +169,12 @@ __device__ inline void load_lds_frag(Frag<T, D>& f, const char* base, int row0, 
   for (int i = 0; i < Frag<T, D>::kChunks; ++i) f.c[i] = *reinterpret_cast<const uint4*>(p + 16 * i);
 }
 
-template <typename T, int D>
+// OUT = false computes only lse (the row statistics): four query subtiles per
+// wavefront, K chunks only, and a running maximum per lane group, merged at the end.
+template <typename T, int D, bool OUT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void attend_kernel(
     PrefillArgs a, int stride, int nblk) {
-  using AT = AttendTile<T, D>;
+  using AT = AttendTile<T, D, OUT>;
   constexpr int QS = AT::QS;
   constexpr int NDT = AT::NDT;
   constexpr float kLow = -1.0e30f;
@@ -265,7 +188,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const int g = lane >> 4;
   const int P = a.P;
   const int qb0 = blk * AT::BQ;
-  const int qw0 = qb0 + (tid >> 6) * AT::ROWS;      // first query of this wavefront
+  const int qw0 = qb0 + __builtin_amdgcn_readfirstlane(tid >> 6) * AT::ROWS;  // first query of this wavefront
   const int qw_last = min(qw0 + AT::ROWS, P) - 1;   // < qw0 when the wavefront has no query
   const int kend = min(P, qb0 + AT::BQ);            // keys the block needs
   const int nch = (kend + AT::KC - 1) / AT::KC;
@@ -287,19 +210,21 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     for (int dt = 0; dt < NDT; ++dt) o[q][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // Chunk loads are unconditional (a clamped address) so the compiler tracks
+  // them exactly and the next chunk stays in flight during the multiply; rows
+  // past the block's keys are replaced by zeros when they are stored.
   uint4 rk[AT::PER_T], rv[AT::PER_T];
-  auto fetch = [&](int ch) {
+  auto fetch = [&](int ch) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < AT::PER_T; ++u) {
-      const int idx = tid + u * kWaves * 64;
-      const int key = ch * AT::KC + idx / (AT::ROWB / 16);
+      const int idx = min(tid + u * kWaves * 64, AT::PIECES - 1);
+      const int key = min(ch * AT::KC + idx / (AT::ROWB / 16), kend - 1);
       const int c16 = idx % (AT::ROWB / 16);
-      const bool in = idx < AT::PIECES && key < kend;
-      rk[u] = in ? load16(Kb + (size_t)key * AT::ROWB + c16 * 16) : make_uint4(0, 0, 0, 0);
-      rv[u] = in ? load16(Vb + (size_t)key * AT::ROWB + c16 * 16) : make_uint4(0, 0, 0, 0);
+      rk[u] = load16(Kb + (size_t)key * AT::ROWB + c16 * 16);
+      if constexpr (OUT) rv[u] = load16(Vb + (size_t)key * AT::ROWB + c16 * 16);
     }
   };
-  auto stash = [&](int b) {
+  auto stash = [&](int ch, int b) __attribute__((always_inline)) {
     char* kl = smem + b * AT::BUF;
     char* vl = kl + AT::KC * AT::KSTR;
 #pragma unroll
@@ -308,13 +233,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       if (idx < AT::PIECES) {
         const int row = idx / (AT::ROWB / 16);
         const int c16 = idx % (AT::ROWB / 16);
-        *reinterpret_cast<uint4*>(kl + row * AT::KSTR + c16 * 16) = rk[u];
-        *reinterpret_cast<uint4*>(vl + row * AT::VSTR + c16 * 16) = rv[u];
+        const bool in = ch * AT::KC + row < kend;
+        *reinterpret_cast<uint4*>(kl + row * AT::KSTR + c16 * 16) = zero_unless(in, rk[u]);
+        if constexpr (OUT) *reinterpret_cast<uint4*>(vl + row * AT::VSTR + c16 * 16) = zero_unless(in, rv[u]);
       }
     }
   };
 
-  auto compute = [&](int ch, const char* kl, const char* vl) {
+  auto compute = [&](int ch, const char* kl, const char* vl) __attribute__((always_inline)) {
     const int c0 = ch * AT::KC;
     f32x4 s[2][QS];
 #pragma unroll
@@ -346,8 +272,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
         mx = fmaxf(mx, fmaxf(fmaxf(s[sub][q][0], s[sub][q][1]), fmaxf(s[sub][q][2], s[sub][q][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if constexpr (OUT) {  // one maximum for the four lane groups of a query
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      }
       const float ms = mx * sc;
       const bool raise = ms > m[q] + kLazy;
       const float mn = raise ? ms : m[q];
@@ -364,6 +292,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
         }
       l[q] = fmaf(l[q], alpha[q], add);
     }
+    if constexpr (!OUT) return;
     if (__any(raise_any)) {
 #pragma unroll
       for (int q = 0; q < QS; ++q)
@@ -406,14 +335,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   };
 
   fetch(0);
-  stash(0);
+  stash(0, 0);
   __syncthreads();
   for (int ch = 0; ch < nch; ++ch) {
     if (ch + 1 < nch) fetch(ch + 1);
     const char* kl = smem + (ch % AT::NBUF) * AT::BUF;
     if (ch * AT::KC <= qw_last) compute(ch, kl, kl + AT::KC * AT::KSTR);  // uniform
     if (AT::NBUF == 1) __syncthreads();
-    if (ch + 1 < nch) stash((ch + 1) % AT::NBUF);
+    if (ch + 1 < nch) stash(ch + 1, (ch + 1) % AT::NBUF);
     __syncthreads();
   }
 
@@ -421,10 +350,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
   for (int q = 0; q < QS; ++q) {
     float lt = l[q];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    if constexpr (OUT) {
+      lt += __shfl_xor(lt, 16, 64);
+      lt += __shfl_xor(lt, 32, 64);
+    } else {  // merge the lane groups' (max, sum)
+#pragma unroll
+      for (int off = 16; off <= 32; off <<= 1) {
+        const float mo = __shfl_xor(m[q], off, 64);
+        const float lo = __shfl_xor(lt, off, 64);
+        const float mn = fmaxf(m[q], mo);
+        lt = lt * fast_exp2(m[q] - mn) + lo * fast_exp2(mo - mn);
+        m[q] = mn;
+      }
+    }
     const int qi = qw0 + q * kTile + (lane & 15);
-    if (qi < P) {
+    if (!OUT && qi < P) {
+      if (g == 0) a.row_lse[(size_t)unit * stride + qi] = m[q] + __log2f(lt);
+    } else if (qi < P) {
       const float inv = 1.f / lt;
       float* orow = a.out + ((size_t)unit * P + qi) * D + 4 * g;
 #pragma unroll
@@ -437,77 +379,125 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   }
 }
 
-// Column sums c_j = sum_{i >= j} exp2(s_ij - lse_i).  A wavefront owns
-// kFixed*16 keys and walks the query subtiles from its first key to the end
-// of the prompt in a fixed order, so the sums are deterministic.  With
-// last_row_only (naive per-step Top-K) only the last prompt row contributes:
-// c_j = exp2(s_{P-1,j} - lse_{P-1}).
+// Column sums c_j = sum_{i >= j} exp2(s_ij - lse_i).  A block's four
+// wavefronts own 4 x kFixed*16 consecutive keys (fixed B operands) and walk the
+// query rows from the block's first key to the end of the prompt in chunks of
+// 32, staged with their lse values through LDS and shared by the wavefronts.
+// Every lane accumulates its columns in a fixed order, so the sums are
+// deterministic.  With last_row_only (naive per-step Top-K) only the last
+// prompt row contributes: c_j = exp2(s_{P-1,j} - lse_{P-1}).
 template <typename T, int D>
-__global__ __launch_bounds__(kWaves * 64) void colsum_kernel(PrefillArgs a, int stride, int nblk) {
-  constexpr int QS = kFixed<T>;
-  constexpr int ROWS = rows_per_wave<T>();
+struct ColTile {
+  static constexpr int QS = kFixed<T>;               // fixed key subtiles per wavefront
+  static constexpr int ROWS = QS * kTile;            // keys per wavefront
+  static constexpr int BK = kWaves * ROWS;           // keys per block
+  static constexpr int QC = 2 * kTile;               // query rows per chunk
+  static constexpr int ROWB = D * Elem<T>::kBytes;
+  static constexpr int QSTR = ROWB + 16;             // 16 rows of one subtile hit distinct banks
+  static constexpr int PIECES = QC * ROWB / 16;
+  static constexpr int PER_T = (PIECES + kWaves * 64 - 1) / (kWaves * 64);
+  static constexpr int BUF = QC * QSTR + QC * 4;     // query rows + their lse
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void colsum_kernel(
+    PrefillArgs a, int stride, int nblk) {
+  using CT = ColTile<T, D>;
+  constexpr int QS = CT::QS;
+  __shared__ __attribute__((aligned(16))) char smem[2 * CT::BUF];
+
   const int id = xcd_local_block(nblk * a.units);
   const int unit = id / nblk;
   const int blk = id % nblk;  // first columns have the most rows
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g4 = (lane >> 4) * 4;
   const int P = a.P;
-  const int j0 = (blk * kWaves + wave) * ROWS;
-  if (j0 >= P) return;
-  constexpr int ROWB = D * Elem<T>::kBytes;
-  const char* Qb = (const char*)a.pq + (size_t)unit * P * ROWB;
-  const char* Kb = (const char*)a.pk + (size_t)unit * P * ROWB;
+  const int jb0 = blk * CT::BK;
+  const int j0 = jb0 + __builtin_amdgcn_readfirstlane(tid >> 6) * CT::ROWS;  // first key of this wavefront
+  const char* Qb = (const char*)a.pq + (size_t)unit * P * CT::ROWB;
+  const char* Kb = (const char*)a.pk + (size_t)unit * P * CT::ROWB;
   const float* lse = a.row_lse + (size_t)unit * stride;
+  const float sc = a.scale_log2;
+  const bool last_only = a.last_row_only != 0;
+  const int q_lo = last_only ? P - 1 : 0;              // first query row that counts
+  const int ch0 = (last_only ? P - 1 : jb0) / CT::QC;  // first chunk the block needs
+  const int nch = (P + CT::QC - 1) / CT::QC;
 
   Frag<T, D> fk[QS];
 #pragma unroll
-  for (int q = 0; q < QS; ++q) fk[q].load(Kb, j0 + q * kTile, P, lane);
-  const int g4 = (lane >> 4) * 4;
+  for (int q = 0; q < QS; ++q) fk[q].load_clamped(Kb, j0 + q * kTile, P, lane);  // keys past P: not written
   float cs[QS];
 #pragma unroll
   for (int q = 0; q < QS; ++q) cs[q] = 0.f;
-  const int nqt = (P + kTile - 1) / kTile;
-  const bool last_only = a.last_row_only != 0;
-  const int qt0 = last_only ? nqt - 1 : j0 / kTile;  // j0 <= P - 1, so j0 / kTile <= nqt - 1
-  const int q_lo = last_only ? P - 1 : 0;          // first query row that counts
 
-  auto step = [&](int qt, const Frag<T, D>& fq, const float4& lq) {
-    const int i0 = qt * kTile;
-    const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
-    // uniform: masking needed
-    const bool edge = last_only || i0 < j0 + ROWS - 1 || i0 + kTile > P;
+  // Unconditional chunk loads (row clamped to P - 1); rows past P are masked.
+  uint4 rq[CT::PER_T];
+  float rl = 0.f;
+  auto fetch = [&](int ch) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      const f32x4 acc = tile_dot<T, D>(fq, fk[q]);
-      const int kj = j0 + q * kTile + (lane & 15);
-      float add = 0.f;
+    for (int u = 0; u < CT::PER_T; ++u) {
+      const int idx = min(tid + u * kWaves * 64, CT::PIECES - 1);
+      const int row = min(ch * CT::QC + idx / (CT::ROWB / 16), P - 1);
+      rq[u] = load16(Qb + (size_t)row * CT::ROWB + (idx % (CT::ROWB / 16)) * 16);
+    }
+    if (tid < CT::QC) rl = lse[min(ch * CT::QC + tid, P - 1)];
+  };
+  auto stash = [&](int b) __attribute__((always_inline)) {
+    char* ql = smem + b * CT::BUF;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(fmaf(acc[i], a.scale_log2, -lv[i]));
-        const int qi = i0 + g4 + i;
-        add += (!edge || (qi >= kj && qi < P && qi >= q_lo)) ? p : 0.f;
+    for (int u = 0; u < CT::PER_T; ++u) {
+      const int idx = tid + u * kWaves * 64;
+      if (idx < CT::PIECES)
+        *reinterpret_cast<uint4*>(ql + (idx / (CT::ROWB / 16)) * CT::QSTR + (idx % (CT::ROWB / 16)) * 16) =
+            rq[u];
+    }
+    if (tid < CT::QC) reinterpret_cast<float*>(ql + CT::QC * CT::QSTR)[tid] = rl;
+  };
+  auto compute = [&](int ch, const char* ql) __attribute__((always_inline)) {
+    const int c0 = ch * CT::QC;
+    const float* ll = reinterpret_cast<const float*>(ql + CT::QC * CT::QSTR);
+    // uniform: some query precedes one of the wavefront's keys, or lies past P
+    const bool edge = last_only || c0 < j0 + CT::ROWS - 1 || c0 + CT::QC > P;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      Frag<T, D> fq;
+      load_lds_frag<T, D>(fq, ql, sub * kTile, CT::QSTR, lane);
+      const float4 lq = *reinterpret_cast<const float4*>(ll + sub * kTile + g4);
+      const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
+#pragma unroll
+      for (int q = 0; q < QS; ++q) {
+        const f32x4 acc = tile_dot<T, D>(fq, fk[q]);  // acc[i]: query 4g + i, key lane % 16
+        float add = 0.f;
+        if (!edge) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) add += fast_exp2(fmaf(acc[i], sc, -lv[i]));
+        } else {
+          // masked terms get the argument -inf (exp2 gives exactly 0), so the
+          // exponential is not turned into a per-lane branch
+          const int kj = j0 + q * kTile + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int qi = c0 + sub * kTile + g4 + i;
+            const bool ok = qi >= kj && qi < P && qi >= q_lo;
+            add += fast_exp2(ok ? fmaf(acc[i], sc, -lv[i]) : -INFINITY);
+          }
+        }
+        cs[q] += add;
       }
-      cs[q] += add;
     }
   };
 
-  Frag<T, D> fa, fb;
-  float4 la, lb;
-  fa.load(Qb, qt0 * kTile, P, lane);
-  la = *reinterpret_cast<const float4*>(lse + qt0 * kTile + g4);
-  for (int qt = qt0; qt < nqt; qt += 2) {
-    if (qt + 1 < nqt) {
-      fb.load(Qb, (qt + 1) * kTile, P, lane);
-      lb = *reinterpret_cast<const float4*>(lse + (qt + 1) * kTile + g4);
-    }
-    step(qt, fa, la);
-    if (qt + 1 < nqt) {
-      if (qt + 2 < nqt) {
-        fa.load(Qb, (qt + 2) * kTile, P, lane);
-        la = *reinterpret_cast<const float4*>(lse + (qt + 2) * kTile + g4);
-      }
-      step(qt + 1, fb, lb);
-    }
+  const int w_last = min(j0 + CT::ROWS, P) - 1;  // last key of this wavefront (< j0: none)
+  fetch(ch0);
+  stash(0);
+  __syncthreads();
+  for (int ch = ch0; ch < nch; ++ch) {
+    if (ch + 1 < nch) fetch(ch + 1);
+    // uniform: skip chunks whose queries all precede the wavefront's keys
+    if (w_last >= j0 && (ch + 1) * CT::QC - 1 >= j0) compute(ch, smem + ((ch - ch0) & 1) * CT::BUF);
+    if (ch + 1 < nch) stash((ch + 1 - ch0) & 1);
+    __syncthreads();
   }
 #pragma unroll
   for (int q = 0; q < QS; ++q) {
@@ -698,24 +688,24 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs 
 
 template <typename T, typename C, int D>
 hipError_t launch_prefill_td(const PrefillArgs& a, int stride, hipStream_t s) {
-  constexpr int rows_per_block = kWaves * rows_per_wave<T>();
-  const int nblk = (a.P + rows_per_block - 1) / rows_per_block;
-  const dim3 grid((unsigned)(nblk * a.units));
+  const dim3 block(kWaves * 64);
   if (a.out) {
-    constexpr int bq = AttendTile<T, D>::BQ;
-    const int nblk_o = (a.P + bq - 1) / bq;
-    hipLaunchKernelGGL((attend_kernel<T, D>), dim3((unsigned)(nblk_o * a.units)), dim3(kWaves * 64), 0, s,
-                       a, stride, nblk_o);
+    constexpr int bq = AttendTile<T, D, true>::BQ;
+    const int nb = (a.P + bq - 1) / bq;
+    hipLaunchKernelGGL((attend_kernel<T, D, true>), dim3((unsigned)(nb * a.units)), block, 0, s, a, stride, nb);
   } else {
-    hipLaunchKernelGGL((rowstats_kernel<T, D>), grid, dim3(kWaves * 64), 0, s, a, stride, nblk);
+    constexpr int bq = AttendTile<T, D, false>::BQ;
+    const int nb = (a.P + bq - 1) / bq;
+    hipLaunchKernelGGL((attend_kernel<T, D, false>), dim3((unsigned)(nb * a.units)), block, 0, s, a, stride, nb);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((colsum_kernel<T, D>), grid, dim3(kWaves * 64), 0, s, a, stride, nblk);
+  constexpr int bk = ColTile<T, D>::BK;
+  const int nbk = (a.P + bk - 1) / bk;
+  hipLaunchKernelGGL((colsum_kernel<T, D>), dim3((unsigned)(nbk * a.units)), block, 0, s, a, stride, nbk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((select_gather_kernel<T, C, D>), dim3(a.units), dim3(kSelThreads), 0, s, a,
-                     stride);
+  hipLaunchKernelGGL((select_gather_kernel<T, C, D>), dim3(a.units), dim3(kSelThreads), 0, s, a, stride);
   return hipGetLastError();
 }
 
