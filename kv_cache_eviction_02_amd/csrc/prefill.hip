@@ -233,14 +233,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       if (idx < AT::PIECES) {
         const int row = idx / (AT::ROWB / 16);
         const int c16 = idx % (AT::ROWB / 16);
-        const bool in = ch * AT::KC + row < kend;
-        *reinterpret_cast<uint4*>(kl + row * AT::KSTR + c16 * 16) = zero_unless(in, rk[u]);
-        if constexpr (OUT) *reinterpret_cast<uint4*>(vl + row * AT::VSTR + c16 * 16) = zero_unless(in, rv[u]);
+        // zeros past the block's keys: only the last chunk can reach them (uniform test)
+        const bool tail = (ch + 1) * AT::KC > kend;
+        const bool in = !tail || ch * AT::KC + row < kend;
+        *reinterpret_cast<uint4*>(kl + row * AT::KSTR + c16 * 16) = tail ? zero_unless(in, rk[u]) : rk[u];
+        if constexpr (OUT)
+          *reinterpret_cast<uint4*>(vl + row * AT::VSTR + c16 * 16) = tail ? zero_unless(in, rv[u]) : rv[u];
       }
     }
   };
 
-  auto compute = [&](int ch, const char* kl, const char* vl) __attribute__((always_inline)) {
+  // mask_tag: 1 = the chunk reaches past the wavefront's first query, 0 = it
+  // does not, 2 = decide at run time.  Row statistics use two instantiations
+  // behind a uniform branch, keeping the mask code out of the common path; the
+  // output variant keeps one body (a second copy of the value product would
+  // not fit the register budget).
+  auto compute = [&](auto mask_tag, int ch, const char* kl, const char* vl) __attribute__((always_inline)) {
+    constexpr int MASK = decltype(mask_tag)::value;
     const int c0 = ch * AT::KC;
     f32x4 s[2][QS];
 #pragma unroll
@@ -250,28 +259,28 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
       for (int q = 0; q < QS; ++q) s[sub][q] = tile_dot<T, D>(fk, fq[q]);
     }
-    if (c0 + AT::KC - 1 > qw0 || c0 + AT::KC > P) {  // uniform: some key is masked
+    // Causal mask.  Keys past P follow every query row < P; rows past P are not
+    // written, so the causal test alone suffices.  Key 16*sub + 4g + i of the
+    // chunk is kept for query qi iff 16*sub + i <= qi - c0 - 4g.
+    if (MASK == 1 || (MASK == 2 && c0 + AT::KC - 1 > qw0)) {
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+      for (int q = 0; q < QS; ++q) {
+        const int t = qw0 + q * kTile + (lane & 15) - c0 - 4 * g;
 #pragma unroll
-        for (int q = 0; q < QS; ++q) {
-          const int qi = qw0 + q * kTile + (lane & 15);
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kj = c0 + sub * kTile + 4 * g + i;
-            s[sub][q][i] = (kj <= qi && kj < P) ? s[sub][q][i] : -INFINITY;
-          }
-        }
+          for (int i = 0; i < 4; ++i) s[sub][q][i] = sub * kTile + i <= t ? s[sub][q][i] : -INFINITY;
+      }
     }
     float alpha[QS];
     bool raise_any = false;
     f32x4 p[2][QS];
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-        mx = fmaxf(mx, fmaxf(fmaxf(s[sub][q][0], s[sub][q][1]), fmaxf(s[sub][q][2], s[sub][q][3])));
+      float mx = fmaxf(s[0][q][0], s[0][q][1]);  // a chain of 3-input maxima
+      mx = fmaxf(fmaxf(mx, s[0][q][2]), s[0][q][3]);
+      mx = fmaxf(fmaxf(mx, s[1][q][0]), s[1][q][1]);
+      mx = fmaxf(fmaxf(mx, s[1][q][2]), s[1][q][3]);
       if constexpr (OUT) {  // one maximum for the four lane groups of a query
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -282,14 +291,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       alpha[q] = fast_exp2(m[q] - mn);
       raise_any |= raise;
       m[q] = mn;
-      float add = 0.f;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[sub][q][i] = fast_exp2(fmaf(s[sub][q][i], sc, -mn));
-          add += p[sub][q][i];
-        }
+        for (int i = 0; i < 4; ++i) p[sub][q][i] = fast_exp2(fmaf(s[sub][q][i], sc, -mn));
+      // pairwise sum: a short dependency chain
+      const float add = ((p[0][q][0] + p[0][q][1]) + (p[0][q][2] + p[0][q][3])) +
+                        ((p[1][q][0] + p[1][q][1]) + (p[1][q][2] + p[1][q][3]));
       l[q] = fmaf(l[q], alpha[q], add);
     }
     if constexpr (!OUT) return;
@@ -340,7 +348,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   for (int ch = 0; ch < nch; ++ch) {
     if (ch + 1 < nch) fetch(ch + 1);
     const char* kl = smem + (ch % AT::NBUF) * AT::BUF;
-    if (ch * AT::KC <= qw_last) compute(ch, kl, kl + AT::KC * AT::KSTR);  // uniform
+    if (ch * AT::KC <= qw_last) {  // uniform
+      if constexpr (OUT)
+        compute(std::integral_constant<int, 2>{}, ch, kl, kl + AT::KC * AT::KSTR);
+      else if (ch * AT::KC + AT::KC - 1 > qw0)
+        compute(std::integral_constant<int, 1>{}, ch, kl, kl + AT::KC * AT::KSTR);
+      else
+        compute(std::integral_constant<int, 0>{}, ch, kl, kl + AT::KC * AT::KSTR);
+    }
     if (AT::NBUF == 1) __syncthreads();
     if (ch + 1 < nch) stash(ch + 1, (ch + 1) % AT::NBUF);
     __syncthreads();
@@ -454,11 +469,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     }
     if (tid < CT::QC) reinterpret_cast<float*>(ql + CT::QC * CT::QSTR)[tid] = rl;
   };
-  auto compute = [&](int ch, const char* ql) __attribute__((always_inline)) {
+  // EDGE (a compile-time tag): some query of the chunk precedes one of the
+  // wavefront's keys or lies past P, or only the last row counts.
+  auto compute = [&](auto edge_tag, int ch, const char* ql) __attribute__((always_inline)) {
+    constexpr bool edge = decltype(edge_tag)::value;
     const int c0 = ch * CT::QC;
     const float* ll = reinterpret_cast<const float*>(ql + CT::QC * CT::QSTR);
-    // uniform: some query precedes one of the wavefront's keys, or lies past P
-    const bool edge = last_only || c0 < j0 + CT::ROWS - 1 || c0 + CT::QC > P;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       Frag<T, D> fq;
@@ -468,21 +484,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
       for (int q = 0; q < QS; ++q) {
         const f32x4 acc = tile_dot<T, D>(fq, fk[q]);  // acc[i]: query 4g + i, key lane % 16
-        float add = 0.f;
-        if (!edge) {
+        float e[4];
+        if constexpr (!edge) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) add += fast_exp2(fmaf(acc[i], sc, -lv[i]));
+          for (int i = 0; i < 4; ++i) e[i] = fast_exp2(fmaf(acc[i], sc, -lv[i]));
         } else {
-          // masked terms get the argument -inf (exp2 gives exactly 0), so the
-          // exponential is not turned into a per-lane branch
-          const int kj = j0 + q * kTile + (lane & 15);
+          // query row base + i counts iff lo <= i < hi (causal, inside the prompt,
+          // and the last row only for the naive policy); masked terms get the
+          // argument -inf (exp2 gives exactly 0), so the exponential is not
+          // turned into a per-lane branch
+          const int base = c0 + sub * kTile + g4;
+          const int lo = max(j0 + q * kTile + (lane & 15), q_lo) - base;
+          const int hi = P - base;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int qi = c0 + sub * kTile + g4 + i;
-            const bool ok = qi >= kj && qi < P && qi >= q_lo;
-            add += fast_exp2(ok ? fmaf(acc[i], sc, -lv[i]) : -INFINITY);
-          }
+          for (int i = 0; i < 4; ++i) e[i] = fast_exp2(i >= lo && i < hi ? fmaf(acc[i], sc, -lv[i]) : -INFINITY);
         }
+        const float add = (e[0] + e[1]) + (e[2] + e[3]);  // pairwise: a short dependency chain
         cs[q] += add;
       }
     }
@@ -495,7 +512,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   for (int ch = ch0; ch < nch; ++ch) {
     if (ch + 1 < nch) fetch(ch + 1);
     // uniform: skip chunks whose queries all precede the wavefront's keys
-    if (w_last >= j0 && (ch + 1) * CT::QC - 1 >= j0) compute(ch, smem + ((ch - ch0) & 1) * CT::BUF);
+    if (w_last >= j0 && (ch + 1) * CT::QC - 1 >= j0) {
+      const int c0 = ch * CT::QC;
+      const char* ql = smem + ((ch - ch0) & 1) * CT::BUF;
+      if (last_only || c0 < j0 + CT::ROWS - 1 || c0 + CT::QC > P)
+        compute(std::true_type{}, ch, ql);
+      else
+        compute(std::false_type{}, ch, ql);
+    }
     if (ch + 1 < nch) stash((ch + 1 - ch0) & 1);
     __syncthreads();
   }
