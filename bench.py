@@ -136,7 +136,7 @@ def cpu_baseline(wl, units_per_worker, steps, policy="h2o"):
 # ---- GPU -----------------------------------------------------------------------
 
 def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, cache="input",
-            policy="h2o"):
+            policy="h2o", streaming=True):
     import torch
     from kv_cache_eviction_02_amd import H2OCache
     from kv_cache_eviction_02_amd.binding import load_library
@@ -152,9 +152,11 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     torch.cuda.synchronize()
     print(f"[bench] staged inputs in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
+    cache_kind = cache
+    # one launch per step, as an autoregressive decoder runs it
     cache = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy, wl.prompt, dtype,
                      wl.scale, device=dev, decode_waves=waves, decode_split=split, cache=cache,
-                     policy=policy)
+                     policy=policy, steps_mode="per_step")
     stream = torch.cuda.current_stream()
     # The first prefill also loads the kernels' code objects; the second one,
     # which rebuilds the same state from the same prompt, is the one timed.
@@ -175,6 +177,7 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     p1.record(stream)
     torch.cuda.synchronize()
     prefill_out_ms = p0.elapsed_time(p1)
+    prompt_keep = prompt if streaming and not single_calls else None
     del prompt, prompt_out
 
     for s in range(warmup):
@@ -196,6 +199,24 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     r1.record(stream)
     torch.cuda.synchronize()
     region_ms = r0.elapsed_time(r1)
+    stream_ms = None
+    if streaming and not single_calls:
+        # the same steps as one persistent launch (known tokens, as in a long-stream run);
+        # h2o_decode_steps picks it by itself for small batches (steps_mode "auto")
+        pc = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy, wl.prompt, dtype,
+                      wl.scale, device=dev, decode_waves=waves, decode_split=split, cache=cache_kind,
+                      policy=policy, steps_mode="persistent")
+        pc.prefill(*prompt_keep)
+        pc.steps(dq[:warmup], dk[:warmup], dv[:warmup])
+        torch.cuda.synchronize()
+        r0.record(stream)
+        pc.steps(dq[warmup:warmup + steps], dk[warmup:warmup + steps], dv[warmup:warmup + steps],
+                 out=out_all, evicted=ev_all)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        stream_ms = r0.elapsed_time(r1)
+        pc.close()
+    del prompt_keep
     if copy_mib:
         # plain device copy of known size, for scaling the HBM byte counters
         x = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -209,7 +230,8 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     if waves == 0:
         waves_used = decode_waves_auto(wl.units)
     cache.close()
-    return dict(region_ms=region_ms, prefill_ms=prefill_ms, prefill_out_ms=prefill_out_ms, waves=waves_used,
+    return dict(region_ms=region_ms, stream_ms=stream_ms, prefill_ms=prefill_ms, prefill_out_ms=prefill_out_ms,
+                waves=waves_used,
                 device=torch.cuda.get_device_name(0))
 
 
@@ -297,7 +319,8 @@ def main():
             "decode_waves": g["waves"],
             "decode_split": args.decode_split or "auto",
             "parallelism": "none",
-            "launch": "h2o_decode_step per step" if args.single_step_calls else "h2o_decode_steps",
+            "launch": ("h2o_decode_step per step" if args.single_step_calls
+                       else "h2o_decode_steps, one launch per step"),
         },
         "roofline": {
             "bound": "hbm",
@@ -321,6 +344,16 @@ def main():
                 "tflops": 2 * prefill_flops(wl) / (g["prefill_out_ms"] * 1e-3) / 1e12,
                 "out_bytes": wl.units * wl.prompt * wl.head_dim * 4,
             },
+        },
+        "streaming": None if g["stream_ms"] is None else {
+            # the same steps over known tokens in one persistent launch
+            "launch": "h2o_decode_steps, one launch for all steps",
+            "kernel": "decode_multi_kernel",
+            "value": 1e3 * steps / g["stream_ms"],
+            "unit": "steps/s",
+            "ms_per_step": g["stream_ms"] / steps,
+            "achieved": bytes_step * steps / (g["stream_ms"] * 1e-3) / 1e9,
+            "frac": bytes_step * steps / (g["stream_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         },
         "cpu_baseline": cpu,
         "device": g["device"],

@@ -95,6 +95,17 @@ typedef enum { H2O_CACHE_INPUT = 0, H2O_CACHE_E4M3 = 1 } h2o_cache_dtype;
  * The heavy-only ablation is recent = 0 under H2O_POLICY_H2O. */
 typedef enum { H2O_POLICY_H2O = 0, H2O_POLICY_STATIC = 1, H2O_POLICY_NAIVE = 2 } h2o_policy;
 
+/* How h2o_decode_steps launches its n steps.  H2O_STEPS_PERSISTENT: one
+ * launch carries every (batch, head) unit through all n steps, keeping its
+ * scores and positions in LDS between steps; it pays off when a step moves
+ * little data (launch and tail latency dominate) and loses to per-step
+ * launches on large batches.  H2O_STEPS_PER_STEP: one launch per step.
+ * H2O_STEPS_AUTO: persistent when the cached K/V rows of one step total at
+ * most 64 MiB, else per step.  Persistent launches also need decode_split = 1
+ * and the unit's 3k + 1 words of LDS; otherwise one launch per step is used.
+ * Results are bit-identical in every mode. */
+typedef enum { H2O_STEPS_AUTO = 0, H2O_STEPS_PER_STEP = 1, H2O_STEPS_PERSISTENT = 2 } h2o_steps_mode;
+
 /* Largest budget k = recent + heavy the decode kernel accepts (its per-row
  * logits live in LDS). */
 #define H2O_MAX_K 8192
@@ -116,6 +127,7 @@ typedef struct {
                           with few units) */
   int32_t cache_dtype; /* h2o_cache_dtype */
   int32_t policy;      /* h2o_policy */
+  int32_t steps_mode;  /* h2o_steps_mode */
 } h2o_config;
 
 typedef struct {

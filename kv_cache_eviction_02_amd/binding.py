@@ -16,6 +16,8 @@ H2O_F32, H2O_BF16 = 0, 1
 H2O_CACHE_INPUT, H2O_CACHE_E4M3 = 0, 1
 H2O_POLICY_H2O, H2O_POLICY_STATIC, H2O_POLICY_NAIVE = 0, 1, 2
 POLICIES = {"h2o": H2O_POLICY_H2O, "static": H2O_POLICY_STATIC, "naive": H2O_POLICY_NAIVE}
+H2O_STEPS_AUTO, H2O_STEPS_PER_STEP, H2O_STEPS_PERSISTENT = 0, 1, 2
+STEPS_MODES = {"auto": H2O_STEPS_AUTO, "per_step": H2O_STEPS_PER_STEP, "persistent": H2O_STEPS_PERSISTENT}
 H2O_MAX_K = 8192
 
 STATUS_NAMES = {
@@ -44,6 +46,7 @@ class h2o_config(ctypes.Structure):
         ("decode_split", ctypes.c_int32),
         ("cache_dtype", ctypes.c_int32),
         ("policy", ctypes.c_int32),
+        ("steps_mode", ctypes.c_int32),
     ]
 
 
@@ -153,7 +156,7 @@ class H2OCache:
 
     def __init__(self, batch, heads, head_dim, recent, heavy, max_prompt, dtype,
                  scale=0.0, device="cuda", decode_waves=0, start_pos=0, start_live=0,
-                 state=None, decode_split=0, cache="input", policy="h2o"):
+                 state=None, decode_split=0, cache="input", policy="h2o", steps_mode="auto"):
         import torch
         self.torch = torch
         load_library()
@@ -161,6 +164,8 @@ class H2OCache:
             raise ValueError("dtype must be torch.float32 or torch.bfloat16")
         if cache not in ("input", "e4m3"):
             raise ValueError("cache must be 'input' or 'e4m3'")
+        if steps_mode not in STEPS_MODES:
+            raise ValueError(f"steps_mode must be one of {sorted(STEPS_MODES)}")
         if policy not in POLICIES:
             raise ValueError(f"policy must be one of {sorted(POLICIES)}")
         self.policy = policy
@@ -198,7 +203,8 @@ class H2OCache:
                               H2O_F32 if dtype == torch.float32 else H2O_BF16, scale,
                               start_pos, start_live, decode_waves, decode_split,
                               H2O_CACHE_E4M3 if cache == "e4m3" else H2O_CACHE_INPUT,
-                              POLICIES[policy])
+                              POLICIES[policy],
+                              STEPS_MODES[steps_mode])
         self.state = h2o_state(self.k_slots.data_ptr(), self.v_slots.data_ptr(),
                                self.score.data_ptr(), self.pos.data_ptr(),
                                self.k_scale.data_ptr() if self.k_scale is not None else None,

@@ -495,27 +495,35 @@ __device__ __forceinline__ void prefetch_scores(const StepView& v, const UnitPtr
   }
 }
 
-template <typename T, typename C, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
-  using GG = Geo<T, C, D, NW>;
+// Workgroup-shared state of one decode step.
+template <typename GG, int D>
+struct StepShared {
+  float s_o[GG::NG][D];
+  float s_m[GG::NG];
+  float s_l[GG::NG];
+  Stash<GG> st;
+  unsigned long long s_key[GG::NT / 64];
+  int s_victim;
+};
+
+// One decode step of one unit by the whole workgroup.  s_logit: LDS, at least
+// n_live + 1 floats.  score_lds / pos_lds: when not null, the unit's scores and
+// positions live in LDS (k entries each) instead of the state buffers.
+template <typename GG, int D>
+__device__ __forceinline__ void unit_step(const DecodeArgs& a, int unit, StepShared<GG, D>& sh, float* s_logit,
+                                          float* score_lds, int32_t* pos_lds) {
   constexpr int EPL = GG::EPL, LPR = GG::LPR, NG = GG::NG, NT = GG::NT, PF = GG::PF;
-
-  __shared__ float s_o[NG][D];
-  __shared__ float s_m[NG];
-  __shared__ float s_l[NG];
-  __shared__ Stash<GG> st;
-  __shared__ unsigned long long s_key[NW];
-  __shared__ int s_victim;
-  extern __shared__ float s_logit[];  // [n_live + 1] logits, later updated scores
-
-  const int unit = blockIdx.x;
   const int tid = threadIdx.x;
   const StepView v(a);
-  const UnitPtrs<GG> u(a, unit, v.k);
+  UnitPtrs<GG> u(a, unit, v.k);
+  if (score_lds) {
+    u.score = score_lds;
+    u.pos = pos_lds;
+  }
   const int gl = (tid & 63) & (GG::G - 1);
   const bool act = gl < LPR;
 
-  if (tid == 0) s_victim = v.fixed_victim();  // overwritten by the argmin owner when the cache is full
+  if (tid == 0) sh.s_victim = v.fixed_victim();  // overwritten by the argmin owner when the cache is full
 
   float qf[EPL];
   load_input<GG>(u.q, act ? gl : 0, qf);
@@ -531,17 +539,70 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  stream_rows<GG>(v, u, 0, v.n_att, qf, a.scale_log2, s_logit, &st, m, lsum, o);
+  stream_rows<GG>(v, u, 0, v.n_att, qf, a.scale_log2, s_logit, &sh.st, m, lsum, o);
 
-  const GroupMerge<NG> gm = merge_groups<GG, D>(m, lsum, o, s_o, s_m, s_l);
+  const GroupMerge<NG> gm = merge_groups<GG, D>(m, lsum, o, sh.s_o, sh.s_m, sh.s_l);
   const float invL = 1.f / gm.L;
   for (int c = tid; c < D; c += NT) {
     float acc = 0.f;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) acc = fmaf(s_o[g][c], gm.wg[g], acc);
+    for (int g = 0; g < NG; ++g) acc = fmaf(sh.s_o[g][c], gm.wg[g], acc);
     a.out[(size_t)unit * D + c] = acc * invL;
   }
-  finish_step<GG>(v, u, gm.M, invL, s_logit, sc_pf, ps_pf, &st, s_key, &s_victim, a.evicted, unit);
+  finish_step<GG>(v, u, gm.M, invL, s_logit, sc_pf, ps_pf, &sh.st, sh.s_key, &sh.s_victim, a.evicted, unit);
+}
+
+template <typename T, typename C, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
+  using GG = Geo<T, C, D, NW>;
+  __shared__ StepShared<GG, D> sh;
+  extern __shared__ float s_logit[];  // [n_live + 1] logits, later updated scores
+  unit_step<GG, D>(a, blockIdx.x, sh, s_logit, nullptr, nullptr);
+}
+
+// n_steps consecutive steps over tokens known in advance, in one launch: each
+// workgroup carries its unit from step to step, so one unit's score update and
+// admission overlap other units' streaming, and the unit's scores and
+// positions stay in LDS until the last step.  `a` describes the first step;
+// live0 = live slots before it.  Inputs of step s start at s * units rows, as
+// do the outputs.  Rows admitted at one step are read at the next by other
+// threads of the same workgroup: the workgroup barrier between steps orders
+// them.
+template <typename T, typename C, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_multi_kernel(DecodeArgs a, int n_steps, int live0) {
+  using GG = Geo<T, C, D, NW>;
+  __shared__ StepShared<GG, D> sh;
+  extern __shared__ float dyn[];  // logits [k + 1], scores [k], positions [k]
+  const int k = a.k;
+  float* s_logit = dyn;
+  float* s_score = dyn + k + 1;
+  int32_t* s_pos = reinterpret_cast<int32_t*>(s_score + k);
+  const int unit = blockIdx.x;
+  const size_t ubase = (size_t)unit * k;
+  for (int i = threadIdx.x; i < k; i += GG::NT) {
+    s_score[i] = a.score[ubase + i];
+    s_pos[i] = a.pos[ubase + i];
+  }
+  __syncthreads();
+  const size_t in_step = (size_t)a.units * GG::IROWB;
+  for (int st = 0; st < n_steps; ++st) {
+    DecodeArgs as = a;
+    as.t = a.t + st;
+    const int n_live = min(live0 + st, k);
+    as.n_ring = min(as.t, a.r);
+    as.n_heavy = n_live - as.n_ring;
+    as.q = (const char*)a.q + st * in_step;
+    as.k_new = (const char*)a.k_new + st * in_step;
+    as.v_new = (const char*)a.v_new + st * in_step;
+    as.out = a.out + (size_t)st * a.units * D;
+    as.evicted = a.evicted ? a.evicted + (size_t)st * a.units : nullptr;
+    unit_step<GG, D>(as, unit, sh, s_logit, s_score, s_pos);
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < k; i += GG::NT) {
+    a.score[ubase + i] = s_score[i];
+    a.pos[ubase + i] = s_pos[i];
+  }
 }
 
 template <typename T, typename C, int D, int NW>
@@ -664,6 +725,35 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
 }
 
 template <typename T, typename C, int D, int NW>
+hipError_t launch_multi_nw(const DecodeArgs& a, int n_steps, int live0, hipStream_t s) {
+  const size_t lds = (size_t)(3 * a.k + 1) * sizeof(float);
+  hipLaunchKernelGGL((decode_multi_kernel<T, C, D, NW>), dim3(a.units), dim3(NW * 64), lds, s, a, n_steps,
+                     live0);
+  return hipGetLastError();
+}
+
+template <typename T, typename C, int D>
+hipError_t launch_multi_d(const DecodeArgs& a, int waves, int n_steps, int live0, hipStream_t s) {
+  switch (waves) {
+    case 1: return launch_multi_nw<T, C, D, 1>(a, n_steps, live0, s);
+    case 2: return launch_multi_nw<T, C, D, 2>(a, n_steps, live0, s);
+    case 4: return launch_multi_nw<T, C, D, 4>(a, n_steps, live0, s);
+    case 8: return launch_multi_nw<T, C, D, 8>(a, n_steps, live0, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, typename C>
+hipError_t launch_multi_t(const DecodeArgs& a, int head_dim, int waves, int n_steps, int live0, hipStream_t s) {
+  switch (head_dim) {
+    case 64: return launch_multi_d<T, C, 64>(a, waves, n_steps, live0, s);
+    case 96: return launch_multi_d<T, C, 96>(a, waves, n_steps, live0, s);
+    case 128: return launch_multi_d<T, C, 128>(a, waves, n_steps, live0, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, typename C, int D, int NW>
 hipError_t launch_nw(const DecodeArgs& a, const SplitScratch* sp, hipStream_t s) {
   const int n_live = a.n_ring + a.n_heavy;
   const size_t lds = (size_t)(n_live + 1) * sizeof(float);
@@ -714,6 +804,47 @@ int decode_split_auto(int units, int waves) {
   (void)units;
   (void)waves;
   return 1;
+}
+
+namespace {
+
+template <typename T, typename C>
+size_t static_lds_t(int head_dim, int waves) {
+  switch (head_dim * 16 + waves) {
+#define H2O_LDS_CASE(D, NW) \
+  case D * 16 + NW: return sizeof(StepShared<Geo<T, C, D, NW>, D>) + 64;
+    H2O_LDS_CASE(64, 1) H2O_LDS_CASE(64, 2) H2O_LDS_CASE(64, 4) H2O_LDS_CASE(64, 8)
+    H2O_LDS_CASE(96, 1) H2O_LDS_CASE(96, 2) H2O_LDS_CASE(96, 4) H2O_LDS_CASE(96, 8)
+    H2O_LDS_CASE(128, 1) H2O_LDS_CASE(128, 2) H2O_LDS_CASE(128, 4) H2O_LDS_CASE(128, 8)
+#undef H2O_LDS_CASE
+    default: return kMaxLds + 1;  // no such instantiation: never fits
+  }
+}
+
+}  // namespace
+
+size_t decode_static_lds(int dtype, int cache, int head_dim, int waves) {
+  // the split kernel holds the same arrays plus one int (the 64-byte margin)
+  if (cache == 1) return static_lds_t<bf16, e4m3>(head_dim, waves);
+  if (dtype == 0) return static_lds_t<float, float>(head_dim, waves);
+  return static_lds_t<bf16, bf16>(head_dim, waves);
+}
+
+bool decode_multi_fits(int k, int dtype, int cache, int head_dim, int waves) {
+  // logits, scores and positions of the unit in LDS: 3k + 1 words
+  return decode_static_lds(dtype, cache, head_dim, waves) + (size_t)(3 * k + 1) * 4 <= kMaxLds;
+}
+
+hipError_t launch_decode_multi(const DecodeArgs& a, int dtype, int cache, int head_dim, int waves, int n_steps,
+                               int live0, hipStream_t s) {
+  if (!decode_multi_fits(a.k, dtype, cache, head_dim, waves)) return hipErrorInvalidValue;
+  if (cache == 1) {
+    if (dtype != 1) return hipErrorInvalidValue;
+    return launch_multi_t<bf16, e4m3>(a, head_dim, waves, n_steps, live0, s);
+  }
+  if (dtype == 0) return launch_multi_t<float, float>(a, head_dim, waves, n_steps, live0, s);
+  if (dtype == 1) return launch_multi_t<bf16, bf16>(a, head_dim, waves, n_steps, live0, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int cache, int head_dim, int waves,

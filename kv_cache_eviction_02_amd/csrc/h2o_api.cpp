@@ -35,6 +35,8 @@ bool valid_dims(const h2o_config* c) {
   return c->batch >= 1 && c->heads >= 1 && c->recent >= 0 && c->heavy >= 0 &&
          (int64_t)c->recent + c->heavy >= 1 &&
          (c->policy == H2O_POLICY_H2O || c->policy == H2O_POLICY_STATIC || c->policy == H2O_POLICY_NAIVE) &&
+         (c->steps_mode == H2O_STEPS_AUTO || c->steps_mode == H2O_STEPS_PER_STEP ||
+          c->steps_mode == H2O_STEPS_PERSISTENT) &&
          c->max_prompt >= 0 && (c->kv_dtype == H2O_F32 || c->kv_dtype == H2O_BF16) &&
          isfinite(c->scale) && c->scale >= 0.f && c->start_pos >= 0 && c->start_live >= 0 &&
          (c->decode_waves == 0 || c->decode_waves == 1 || c->decode_waves == 2 ||
@@ -88,6 +90,16 @@ h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** o
   c->st = *state;
   c->k = (int32_t)k;
   c->waves = cfg->decode_waves ? cfg->decode_waves : h2o::decode_waves_auto((int)units);
+  // the single-step kernels keep k + 1 logits in LDS beside their static arrays
+  auto lds_ok = [&](int w) {
+    return h2o::decode_static_lds(cfg->kv_dtype, cfg->cache_dtype, cfg->head_dim, w) + (size_t)(k + 1) * 4 <=
+           h2o::kMaxLds;
+  };
+  while (!cfg->decode_waves && c->waves > 1 && !lds_ok(c->waves)) c->waves /= 2;
+  if (!lds_ok(c->waves)) {
+    delete c;
+    return H2O_ERR_UNSUPPORTED;
+  }
   const float scale = cfg->scale > 0.f ? cfg->scale : 1.f / sqrtf((float)cfg->head_dim);
   c->scale_log2 = scale * kLog2e;
   c->t = t0;
@@ -173,9 +185,9 @@ h2o_status h2o_prefill_with_output(h2o_ctx* ctx, const void* q, const void* k, c
 
 namespace {
 
-// Enqueue one decode step at the ctx's current position and advance it.
-h2o_status enqueue_step(h2o_ctx* ctx, const void* q, const void* k_new, const void* v_new,
-                        float* out, int32_t* evicted_pos, hipStream_t stream) {
+// Kernel arguments of the step at the ctx's current position.
+h2o::DecodeArgs step_args(const h2o_ctx* ctx, const void* q, const void* k_new, const void* v_new, float* out,
+                          int32_t* evicted_pos) {
   const int32_t r = ctx->cfg.recent;
   const int32_t n_ring = ctx->t < r ? ctx->t : r;
   h2o::DecodeArgs a;
@@ -198,6 +210,13 @@ h2o_status enqueue_step(h2o_ctx* ctx, const void* q, const void* k_new, const vo
   a.n_heavy = ctx->n_live - n_ring;
   a.scale_log2 = ctx->scale_log2;
   a.policy = ctx->cfg.policy;
+  return a;
+}
+
+// Enqueue one decode step at the ctx's current position and advance it.
+h2o_status enqueue_step(h2o_ctx* ctx, const void* q, const void* k_new, const void* v_new,
+                        float* out, int32_t* evicted_pos, hipStream_t stream) {
+  const h2o::DecodeArgs a = step_args(ctx, q, k_new, v_new, out, evicted_pos);
   const hipError_t e = h2o::launch_decode(a, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype,
                                           ctx->cfg.head_dim, ctx->waves, &ctx->split, stream);
   if (e != hipSuccess) return from_hip(e);
@@ -229,6 +248,23 @@ h2o_status h2o_decode_steps(h2o_ctx* ctx, int32_t n_steps, const void* q, const 
   if (!ctx || n_steps < 1 || !step_args_ok(q, k_new, v_new, out, evicted_pos)) return H2O_ERR_INVALID;
   if (!ctx->has_state) return H2O_ERR_STATE;
   if ((int64_t)ctx->t + n_steps >= INT32_MAX - 1) return H2O_ERR_STATE;
+  // cached K/V bytes one step streams, for the automatic choice
+  const size_t row_bytes = (size_t)ctx->cfg.head_dim *
+                           (ctx->cfg.cache_dtype == H2O_CACHE_E4M3 ? 1 : ctx->cfg.kv_dtype == H2O_BF16 ? 2 : 4);
+  const size_t step_bytes = (size_t)ctx->cfg.batch * ctx->cfg.heads * ctx->k * 2 * row_bytes;
+  const bool persistent = ctx->cfg.steps_mode == H2O_STEPS_PERSISTENT ||
+                          (ctx->cfg.steps_mode == H2O_STEPS_AUTO && step_bytes <= ((size_t)64 << 20));
+  if (n_steps > 1 && persistent && ctx->split.splits < 2 &&
+      h2o::decode_multi_fits(ctx->k, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype, ctx->cfg.head_dim, ctx->waves)) {
+    // one launch carries every unit through all n_steps
+    const h2o::DecodeArgs a = step_args(ctx, q, k_new, v_new, out, evicted_pos);
+    const hipError_t e = h2o::launch_decode_multi(a, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype, ctx->cfg.head_dim,
+                                                  ctx->waves, n_steps, ctx->n_live, (hipStream_t)stream);
+    if (e != hipSuccess) return from_hip(e);
+    ctx->t += n_steps;
+    ctx->n_live = (int64_t)ctx->n_live + n_steps < ctx->k ? ctx->n_live + n_steps : ctx->k;
+    return H2O_OK;
+  }
   const size_t units = (size_t)ctx->cfg.batch * ctx->cfg.heads;
   const size_t in_step = units * ctx->cfg.head_dim * (ctx->cfg.kv_dtype == H2O_BF16 ? 2 : 4);
   const size_t out_step = units * ctx->cfg.head_dim;

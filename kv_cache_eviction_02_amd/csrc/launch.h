@@ -64,6 +64,20 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int cache, int head_dim
                          const SplitScratch* sp, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int cache, int head_dim, hipStream_t s);
 
+// n_steps consecutive steps in one launch (one workgroup per unit, no split):
+// `a` describes the first step, live0 = live slots before it; inputs and
+// outputs of step s start s * units rows further.  Requires
+// decode_multi_fits(a.k, ...).
+hipError_t launch_decode_multi(const DecodeArgs& a, int dtype, int cache, int head_dim, int waves, int n_steps,
+                               int live0, hipStream_t s);
+
+// LDS a workgroup may take without opting in to more.
+constexpr size_t kMaxLds = 64 * 1024;
+// Static LDS of the decode kernels for this instantiation; the single-step
+// kernels add (live slots + 1) * 4 bytes, the multi-step kernel (3k + 1) * 4.
+size_t decode_static_lds(int dtype, int cache, int head_dim, int waves);
+bool decode_multi_fits(int k, int dtype, int cache, int head_dim, int waves);
+
 // Automatic wavefronts per unit for the decode kernel.
 int decode_waves_auto(int units);
 // Automatic workgroups per unit (1 = no split).

@@ -25,7 +25,7 @@ def header_functions():
 def cfg(**kw):
     base = dict(batch=2, heads=3, head_dim=64, recent=4, heavy=4, max_prompt=0,
                 kv_dtype=B.H2O_BF16, scale=0.0, start_pos=0, start_live=0, decode_waves=0,
-                decode_split=0, cache_dtype=0, policy=0)
+                decode_split=0, cache_dtype=0, policy=0, steps_mode=0)
     base.update(kw)
     return B.h2o_config(**base)
 
@@ -55,10 +55,10 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stdio.h>
 #include "h2o.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(h2o_config), offsetof(h2o_config, scale),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(h2o_config), offsetof(h2o_config, scale),
          offsetof(h2o_config, decode_waves), sizeof(h2o_state), offsetof(h2o_state, pos),
          offsetof(h2o_config, decode_split), offsetof(h2o_config, cache_dtype),
-         offsetof(h2o_state, v_scale), offsetof(h2o_config, policy));
+         offsetof(h2o_state, v_scale), offsetof(h2o_config, policy), offsetof(h2o_config, steps_mode));
   printf("%d %d %d\n", H2O_POLICY_H2O, H2O_POLICY_STATIC, H2O_POLICY_NAIVE);
   printf("%d\n", H2O_MAX_K);
   return 0;
@@ -71,7 +71,7 @@ int main(void) {
                    B.h2o_config.decode_waves.offset, ctypes.sizeof(B.h2o_state),
                    B.h2o_state.pos.offset, B.h2o_config.decode_split.offset,
                    B.h2o_config.cache_dtype.offset, B.h2o_state.v_scale.offset,
-                   B.h2o_config.policy.offset]
+                   B.h2o_config.policy.offset, B.h2o_config.steps_mode.offset]
     assert list(map(int, lines[1].split())) == [B.H2O_POLICY_H2O, B.H2O_POLICY_STATIC,
                                                 B.H2O_POLICY_NAIVE]
     assert int(lines[2]) == B.H2O_MAX_K
@@ -90,6 +90,7 @@ def test_status_strings():
     (dict(recent=0, heavy=0), B.H2O_ERR_INVALID),                   # empty budget
     (dict(policy=3), B.H2O_ERR_INVALID),
     (dict(policy=-1), B.H2O_ERR_INVALID),
+    (dict(steps_mode=3), B.H2O_ERR_INVALID),
     (dict(heavy=-1), B.H2O_ERR_INVALID),
     (dict(max_prompt=-5), B.H2O_ERR_INVALID),
     (dict(kv_dtype=7), B.H2O_ERR_INVALID),
@@ -204,3 +205,18 @@ def test_create_accepts_policies_and_heavy_only(policy):
         assert st == B.H2O_OK and ctx
         assert k2.h2o_query(ctx) == (B.H2O_OK, kw.get("start_pos", 0), kw.get("start_live", 0))
         assert k2.h2o_destroy(ctx) == B.H2O_OK
+
+
+def test_lds_budget_of_large_e4m3_budget():
+    # k = 8192 with E4M3 rows: eight wavefronts per unit would need more than the
+    # 64 KB of LDS a workgroup gets (static row-group arrays plus k + 1 logits);
+    # the automatic choice drops to fewer wavefronts, an explicit 8 is refused.
+    base = dict(batch=1, heads=2, head_dim=128, recent=4096, heavy=4096, cache_dtype=1)
+    st, ctx = k2.h2o_create(cfg(**base), state(ks=FAKE, vs=FAKE))
+    assert st == B.H2O_OK and ctx
+    assert k2.h2o_destroy(ctx) == B.H2O_OK
+    st, ctx = k2.h2o_create(cfg(decode_waves=8, **base), state(ks=FAKE, vs=FAKE))
+    assert st == B.H2O_ERR_UNSUPPORTED and ctx is None
+    st, ctx = k2.h2o_create(cfg(decode_waves=4, **base), state(ks=FAKE, vs=FAKE))
+    assert st == B.H2O_OK and ctx
+    assert k2.h2o_destroy(ctx) == B.H2O_OK
