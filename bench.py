@@ -259,6 +259,8 @@ def main():
     ap.add_argument("--decode-split", type=int, default=0,
                     help="decode workgroups per (batch, head) unit; 0 = library default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-streaming", action="store_true",
+                    help="skip the persistent-launch timing of the same steps")
     ap.add_argument("--single-step-calls", action="store_true",
                     help="one h2o_decode_step call per step instead of one h2o_decode_steps call")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -291,7 +293,7 @@ def main():
     if args.cache == "e4m3" and wl.kv_dtype != "bf16":
         sys.exit("an E4M3 cache takes bf16 inputs")
     g = run_gpu(wl, steps, warmup, args.decode_waves, args.copy_calibration_mib, args.single_step_calls,
-                args.decode_split, args.cache, args.policy)
+                args.decode_split, args.cache, args.policy, not args.no_streaming)
     ms_per_step = g["region_ms"] / steps
     # one decode launch per step: the mean launch duration over the timed region
     mean_launch_ms = ms_per_step
