@@ -605,7 +605,6 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs 
   constexpr int GW = RC::GW;
   __shared__ int hist[256];
   __shared__ int buf[kSelThreads];
-  __shared__ int s_slot[kSelThreads];
   __shared__ int s_digit, s_need;
 
   const int unit = blockIdx.x;
@@ -621,7 +620,9 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs 
   int32_t* pos = a.pos + (size_t)unit * k;
 
   // Radix select (4 x 8 bits) of the h-th largest score bit pattern among the
-  // pool; scores are >= 0 so their bits order like the values.
+  // pool; scores are >= 0 so their bits order like the values.  Each pass
+  // histograms one byte among the patterns matching the prefix so far; a scan
+  // over the bins from the top finds the bin holding the need-th largest.
   uint32_t thr = 0;
   int need = 0;
   if (!keep_all && h > 0) {
@@ -636,16 +637,13 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs 
         if ((b & mask) == prefix) atomicAdd(&hist[(b >> shift) & 255], 1);
       }
       __syncthreads();
-      if (tid == 0) {
-        int cum = 0;
-        for (int d = 255; d >= 0; --d) {
-          if (cum + hist[d] >= need) {
-            s_digit = d;
-            s_need = need - cum;
-            break;
-          }
-          cum += hist[d];
-        }
+      // thread t looks at bin 255 - t: count above it (exclusive) and with it
+      const int cnt = hist[255 - tid];
+      int tot;
+      const int above = block_exclusive_scan(cnt, buf, &tot);
+      if (above < need && above + cnt >= need) {  // exactly one thread
+        s_digit = 255 - tid;
+        s_need = need - above;
       }
       __syncthreads();
       prefix |= (uint32_t)s_digit << shift;
@@ -674,20 +672,11 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs 
     const int sel_rank = sel_seen + block_exclusive_scan(sel ? 1 : 0, buf, &sel_total);
     eq_seen += eq_total;
     sel_seen += sel_total;
-    const int slot = sel ? r + (n_sel - 1 - sel_rank) : -1;
-    s_slot[tid] = slot;
     if (sel) {
+      const int slot = r + (n_sel - 1 - sel_rank);
       score[slot] = c[p];
       pos[slot] = p;
     }
-    __syncthreads();
-    // GW consecutive lanes per row: whole groups are in or out of the loop together
-    for (int idx = tid; idx < kSelThreads * GW; idx += kSelThreads) {
-      const int x = idx / GW;
-      const int sl = s_slot[x];
-      if (sl >= 0) RC::item(a, unit, P, k, hi - 1 - x, sl, idx % GW);
-    }
-    __syncthreads();
   }
 
   // Protected window: the newest n_ring prompt positions, slot = position % r.
@@ -696,16 +685,58 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs 
     score[p % r] = c[p];
     pos[p % r] = p;
   }
-  for (int idx = tid; idx < n_ring * GW; idx += kSelThreads) {
-    const int p = P - n_ring + idx / GW;
-    RC::item(a, unit, P, k, p, p % r, idx % GW);
-  }
   // Unused slots.
   for (int s = tid; s < k; s += kSelThreads) {
     const bool used = s < r ? s < n_ring : s < r + n_sel;
     if (!used) {
       score[s] = 0.f;
       pos[s] = -1;
+    }
+  }
+  __syncthreads();  // the positions just written are read back below
+
+  // Row copies: the used slots in order (ring, then heavy), GW consecutive
+  // lanes per row, each slot's source position read back from pos.  For an
+  // unquantized cache every thread first issues the loads of up to kBatch
+  // items, then their stores, so many rows are in flight at once.
+  const int n_rows = n_ring + n_sel;
+  const int n_items = n_rows * GW;
+  auto slot_of_row = [&](int row) { return row < n_ring ? row : r + (row - n_ring); };
+  if constexpr (!RC::kQuant) {
+    constexpr int kBatch = 4;
+    constexpr int IROWB = RC::IROWB;
+    const char* __restrict__ Kb = (const char*)a.pk + (size_t)unit * P * IROWB;
+    const char* __restrict__ Vb = (const char*)a.pv + (size_t)unit * P * IROWB;
+    char* __restrict__ Ks = (char*)a.k_slots + (size_t)unit * k * RC::CROWB;
+    char* __restrict__ Vs = (char*)a.v_slots + (size_t)unit * k * RC::CROWB;
+    for (int base = 0; base < n_items; base += kSelThreads * kBatch) {
+      uint4 kx[kBatch], vx[kBatch];
+      int dst[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int idx = min(base + u * kSelThreads + tid, n_items - 1);  // clamped: loads stay in range
+        const int sl = slot_of_row(idx / GW);
+        const int cc = idx % GW;
+        const size_t src = (size_t)pos[sl] * IROWB + cc * 16;
+        kx[u] = load16(Kb + src);
+        vx[u] = load16(Vb + src);
+        dst[u] = sl * RC::CROWB + cc * 16;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (base + u * kSelThreads + tid < n_items) {
+          store16(Ks + dst[u], kx[u]);
+          store16(Vs + dst[u], vx[u]);
+        }
+      }
+    }
+  } else {
+    for (int idx = tid; idx < ((n_items + kSelThreads - 1) / kSelThreads) * kSelThreads; idx += kSelThreads) {
+      // whole GW-lane groups are in or out together (GW divides kSelThreads)
+      if (idx < n_items) {
+        const int sl = slot_of_row(idx / GW);
+        RC::item(a, unit, P, k, pos[sl], sl, idx % GW);
+      }
     }
   }
 }
