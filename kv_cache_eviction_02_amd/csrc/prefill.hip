@@ -394,16 +394,186 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   }
 }
 
+// Row statistics lse_i = m_i + log2(sum_{j <= i} exp2(s_ij - m_i)), software
+// pipelined: a block's four wavefronts own 4 x RowTile::QS * 16 queries and
+// walk the keys in chunks of 32 staged through LDS (double-buffered, shared by
+// the wavefronts).  At chunk c a wavefront issues the MFMAs of chunk c + 1 and
+// then runs the exponentials of chunk c from registers, so the matrix and
+// vector pipes overlap inside the wavefront.  The running maximum is kept per
+// lane group and raised only when a chunk exceeds it by more than kLazy; the
+// four lane groups of a query merge their (max, sum) at the end.
+#ifndef H2O_ROW_QS
+#define H2O_ROW_QS 2
+#endif
+template <typename T, int D>
+struct RowTile {
+  static constexpr int QS = sizeof(T) == 2 ? H2O_ROW_QS : 2;  // fixed query subtiles per wavefront
+  static constexpr int ROWS = QS * kTile;
+  static constexpr int BQ = kWaves * ROWS;
+  static constexpr int KC = 2 * kTile;
+  static constexpr int ROWB = D * Elem<T>::kBytes;
+  static constexpr int KSTR = ROWB + 16;
+  static constexpr int PIECES = KC * ROWB / 16;
+  static constexpr int PER_T = (PIECES + kWaves * 64 - 1) / (kWaves * 64);
+  static constexpr int BUF = KC * KSTR;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void rowstats_kernel(
+    PrefillArgs a, int stride, int nblk) {
+  using RT = RowTile<T, D>;
+  constexpr int QS = RT::QS;
+  constexpr float kLow = -1.0e30f;
+  __shared__ __attribute__((aligned(16))) char smem[2 * RT::BUF];
+
+  const int id = xcd_local_block(nblk * a.units);
+  const int unit = id / nblk;
+  const int blk = nblk - 1 - id % nblk;  // longest rows first
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int P = a.P;
+  const int qb0 = blk * RT::BQ;
+  const int qw0 = qb0 + __builtin_amdgcn_readfirstlane(tid >> 6) * RT::ROWS;
+  const int qw_last = min(qw0 + RT::ROWS, P) - 1;  // < qw0 when the wavefront has no query
+  const int kend = min(P, qb0 + RT::BQ);
+  const int nch = (kend + RT::KC - 1) / RT::KC;
+  const char* Qb = (const char*)a.pq + (size_t)unit * P * RT::ROWB;
+  const char* Kb = (const char*)a.pk + (size_t)unit * P * RT::ROWB;
+  const float sc = a.scale_log2;
+
+  Frag<T, D> fq[QS];
+#pragma unroll
+  for (int q = 0; q < QS; ++q) fq[q].load_clamped(Qb, qw0 + q * kTile, P, lane);  // rows past P: not written
+  float m[QS], l[QS];
+#pragma unroll
+  for (int q = 0; q < QS; ++q) {
+    m[q] = kLow;
+    l[q] = 0.f;
+  }
+
+  uint4 rk[RT::PER_T];
+  auto fetch = [&](int ch) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < RT::PER_T; ++u) {
+      const int idx = min(tid + u * kWaves * 64, RT::PIECES - 1);
+      const int key = min(ch * RT::KC + idx / (RT::ROWB / 16), kend - 1);
+      rk[u] = load16(Kb + (size_t)key * RT::ROWB + (idx % (RT::ROWB / 16)) * 16);
+    }
+  };
+  auto stash = [&](int b) __attribute__((always_inline)) {
+    char* kl = smem + b * RT::BUF;
+#pragma unroll
+    for (int u = 0; u < RT::PER_T; ++u) {
+      const int idx = tid + u * kWaves * 64;
+      if (idx < RT::PIECES)
+        *reinterpret_cast<uint4*>(kl + (idx / (RT::ROWB / 16)) * RT::KSTR + (idx % (RT::ROWB / 16)) * 16) = rk[u];
+    }
+  };
+  // Keys past kend hold copies of row kend - 1: they follow every query of the
+  // block that is < P, so the causal mask removes them.
+  auto mult = [&](int ch, f32x4 (&s)[2][QS]) __attribute__((always_inline)) {
+    const char* kl = smem + (ch & 1) * RT::BUF;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      Frag<T, D> fk;
+      load_lds_frag<T, D>(fk, kl, sub * kTile, RT::KSTR, lane);
+#pragma unroll
+      for (int q = 0; q < QS; ++q) s[sub][q] = tile_dot<T, D>(fk, fq[q]);
+    }
+  };
+  auto soft = [&](auto mask_tag, int ch, f32x4 (&s)[2][QS]) __attribute__((always_inline)) {
+    if constexpr (decltype(mask_tag)::value) {
+      // key 16*sub + 4g + i of the chunk is kept for query qi iff 16*sub + i <= qi - c0 - 4g
+#pragma unroll
+      for (int q = 0; q < QS; ++q) {
+        const int t = qw0 + q * kTile + (lane & 15) - ch * RT::KC - 4 * g;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[sub][q][i] = sub * kTile + i <= t ? s[sub][q][i] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      float mx = fmaxf(s[0][q][0], s[0][q][1]);
+      mx = fmaxf(fmaxf(mx, s[0][q][2]), s[0][q][3]);
+      mx = fmaxf(fmaxf(mx, s[1][q][0]), s[1][q][1]);
+      mx = fmaxf(fmaxf(mx, s[1][q][2]), s[1][q][3]);
+      const float ms = mx * sc;
+      const float mn = ms > m[q] + kLazy ? ms : m[q];
+      const float alpha = fast_exp2(m[q] - mn);
+      m[q] = mn;
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(s[i >> 2][q][i & 3], sc, -mn));
+      const float add = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      l[q] = fmaf(l[q], alpha, add);
+    }
+  };
+  auto active = [&](int ch) { return ch < nch && ch * RT::KC <= qw_last; };  // uniform
+  // one pipeline stage: MFMAs of chunk ch + 1 into nxt, exponentials of chunk ch from cur
+  auto stage = [&](int ch, f32x4 (&cur)[2][QS], f32x4 (&nxt)[2][QS]) __attribute__((always_inline)) {
+    if (ch + 2 < nch) fetch(ch + 2);
+    if (active(ch + 1)) mult(ch + 1, nxt);
+    if (active(ch)) {
+      if (ch * RT::KC + RT::KC - 1 > qw0)
+        soft(std::true_type{}, ch, cur);
+      else
+        soft(std::false_type{}, ch, cur);
+    }
+    if (ch + 2 < nch) stash(ch & 1);  // chunk ch + 2 replaces chunk ch, read one stage ago
+    __syncthreads();
+  };
+
+  f32x4 sa[2][QS], sb[2][QS];
+  fetch(0);
+  stash(0);
+  if (nch > 1) {
+    fetch(1);
+    stash(1);
+  }
+  __syncthreads();
+  if (active(0)) mult(0, sa);
+  __syncthreads();  // every wavefront has read chunk 0 before chunk 2 replaces it
+  for (int ch = 0; ch < nch; ch += 2) {
+    stage(ch, sa, sb);
+    if (ch + 1 < nch) stage(ch + 1, sb, sa);
+  }
+
+  if (qw0 >= P) return;
+#pragma unroll
+  for (int q = 0; q < QS; ++q) {
+    float lt = l[q];
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {  // merge the lane groups' (max, sum)
+      const float mo = __shfl_xor(m[q], off, 64);
+      const float lo = __shfl_xor(lt, off, 64);
+      const float mn = fmaxf(m[q], mo);
+      lt = lt * fast_exp2(m[q] - mn) + lo * fast_exp2(mo - mn);
+      m[q] = mn;
+    }
+    const int qi = qw0 + q * kTile + (lane & 15);
+    if (g == 0 && qi < P) a.row_lse[(size_t)unit * stride + qi] = m[q] + __log2f(lt);
+  }
+}
+
 // Column sums c_j = sum_{i >= j} exp2(s_ij - lse_i).  A block's four
-// wavefronts own 4 x kFixed*16 consecutive keys (fixed B operands) and walk the
-// query rows from the block's first key to the end of the prompt in chunks of
-// 32, staged with their lse values through LDS and shared by the wavefronts.
-// Every lane accumulates its columns in a fixed order, so the sums are
-// deterministic.  With last_row_only (naive per-step Top-K) only the last
-// prompt row contributes: c_j = exp2(s_{P-1,j} - lse_{P-1}).
+// wavefronts own 4 x ColTile::QS * 16 consecutive keys (fixed B operands) and
+// walk the query rows from the block's first key to the end of the prompt in
+// chunks of 32, staged with their lse values through LDS (double-buffered,
+// shared by the wavefronts).  Software pipelined like the row statistics: at
+// chunk c a wavefront issues the MFMAs of chunk c + 1 (and reads its lse into
+// registers), then runs the exponentials of chunk c.  Every lane accumulates
+// its columns in a fixed order, so the sums are deterministic.  With
+// last_row_only (naive per-step Top-K) only the last prompt row contributes:
+// c_j = exp2(s_{P-1,j} - lse_{P-1}).
+#ifndef H2O_COL_QS
+#define H2O_COL_QS 2
+#endif
 template <typename T, int D>
 struct ColTile {
-  static constexpr int QS = kFixed<T>;               // fixed key subtiles per wavefront
+  static constexpr int QS = sizeof(T) == 2 ? H2O_COL_QS : 2;  // fixed key subtiles per wavefront
   static constexpr int ROWS = QS * kTile;            // keys per wavefront
   static constexpr int BK = kWaves * ROWS;           // keys per block
   static constexpr int QC = 2 * kTile;               // query rows per chunk
@@ -438,6 +608,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const int q_lo = last_only ? P - 1 : 0;              // first query row that counts
   const int ch0 = (last_only ? P - 1 : jb0) / CT::QC;  // first chunk the block needs
   const int nch = (P + CT::QC - 1) / CT::QC;
+  const int w_last = min(j0 + CT::ROWS, P) - 1;       // last key of this wavefront (< j0: none)
 
   Frag<T, D> fk[QS];
 #pragma unroll
@@ -469,25 +640,33 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     }
     if (tid < CT::QC) reinterpret_cast<float*>(ql + CT::QC * CT::QSTR)[tid] = rl;
   };
-  // EDGE (a compile-time tag): some query of the chunk precedes one of the
-  // wavefront's keys or lies past P, or only the last row counts.
-  auto compute = [&](auto edge_tag, int ch, const char* ql) __attribute__((always_inline)) {
-    constexpr bool edge = decltype(edge_tag)::value;
-    const int c0 = ch * CT::QC;
+  // S tiles of a chunk (acc[i]: query 4g + i of the subtile, key lane % 16) and the
+  // chunk's lse, both into registers: the buffer is refilled one stage later.
+  auto mult = [&](int ch, f32x4 (&s)[2][QS], float4 (&lq)[2]) __attribute__((always_inline)) {
+    const char* ql = smem + ((ch - ch0) & 1) * CT::BUF;
     const float* ll = reinterpret_cast<const float*>(ql + CT::QC * CT::QSTR);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       Frag<T, D> fq;
       load_lds_frag<T, D>(fq, ql, sub * kTile, CT::QSTR, lane);
-      const float4 lq = *reinterpret_cast<const float4*>(ll + sub * kTile + g4);
-      const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
+      lq[sub] = *reinterpret_cast<const float4*>(ll + sub * kTile + g4);
+#pragma unroll
+      for (int q = 0; q < QS; ++q) s[sub][q] = tile_dot<T, D>(fq, fk[q]);
+    }
+  };
+  auto soft = [&](auto edge_tag, int ch, const f32x4 (&s)[2][QS], const float4 (&lq)[2])
+                  __attribute__((always_inline)) {
+    constexpr bool edge = decltype(edge_tag)::value;
+    const int c0 = ch * CT::QC;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const float lv[4] = {lq[sub].x, lq[sub].y, lq[sub].z, lq[sub].w};
 #pragma unroll
       for (int q = 0; q < QS; ++q) {
-        const f32x4 acc = tile_dot<T, D>(fq, fk[q]);  // acc[i]: query 4g + i, key lane % 16
         float e[4];
         if constexpr (!edge) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) e[i] = fast_exp2(fmaf(acc[i], sc, -lv[i]));
+          for (int i = 0; i < 4; ++i) e[i] = fast_exp2(fmaf(s[sub][q][i], sc, -lv[i]));
         } else {
           // query row base + i counts iff lo <= i < hi (causal, inside the prompt,
           // and the last row only for the naive policy); masked terms get the
@@ -497,31 +676,43 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
           const int lo = max(j0 + q * kTile + (lane & 15), q_lo) - base;
           const int hi = P - base;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) e[i] = fast_exp2(i >= lo && i < hi ? fmaf(acc[i], sc, -lv[i]) : -INFINITY);
+          for (int i = 0; i < 4; ++i) e[i] = fast_exp2(i >= lo && i < hi ? fmaf(s[sub][q][i], sc, -lv[i]) : -INFINITY);
         }
-        const float add = (e[0] + e[1]) + (e[2] + e[3]);  // pairwise: a short dependency chain
-        cs[q] += add;
+        cs[q] += (e[0] + e[1]) + (e[2] + e[3]);  // pairwise: a short dependency chain
       }
     }
   };
+  // uniform: the wavefront has keys and the chunk has a query at or after its first key
+  auto active = [&](int ch) { return ch < nch && w_last >= j0 && (ch + 1) * CT::QC - 1 >= j0; };
+  auto stage = [&](int ch, f32x4 (&cur)[2][QS], float4 (&lcur)[2], f32x4 (&nxt)[2][QS], float4 (&lnxt)[2])
+                   __attribute__((always_inline)) {
+    if (ch + 2 < nch) fetch(ch + 2);
+    if (active(ch + 1)) mult(ch + 1, nxt, lnxt);
+    if (active(ch)) {
+      const int c0 = ch * CT::QC;
+      if (last_only || c0 < j0 + CT::ROWS - 1 || c0 + CT::QC > P)
+        soft(std::true_type{}, ch, cur, lcur);
+      else
+        soft(std::false_type{}, ch, cur, lcur);
+    }
+    if (ch + 2 < nch) stash((ch - ch0) & 1);  // chunk ch + 2 replaces chunk ch, read one stage ago
+    __syncthreads();
+  };
 
-  const int w_last = min(j0 + CT::ROWS, P) - 1;  // last key of this wavefront (< j0: none)
+  f32x4 sa[2][QS], sb[2][QS];
+  float4 la[2], lb[2];
   fetch(ch0);
   stash(0);
+  if (ch0 + 1 < nch) {
+    fetch(ch0 + 1);
+    stash(1);
+  }
   __syncthreads();
-  for (int ch = ch0; ch < nch; ++ch) {
-    if (ch + 1 < nch) fetch(ch + 1);
-    // uniform: skip chunks whose queries all precede the wavefront's keys
-    if (w_last >= j0 && (ch + 1) * CT::QC - 1 >= j0) {
-      const int c0 = ch * CT::QC;
-      const char* ql = smem + ((ch - ch0) & 1) * CT::BUF;
-      if (last_only || c0 < j0 + CT::ROWS - 1 || c0 + CT::QC > P)
-        compute(std::true_type{}, ch, ql);
-      else
-        compute(std::false_type{}, ch, ql);
-    }
-    if (ch + 1 < nch) stash((ch + 1 - ch0) & 1);
-    __syncthreads();
+  if (active(ch0)) mult(ch0, sa, la);
+  __syncthreads();  // every wavefront has read the first chunk before the third replaces it
+  for (int ch = ch0; ch < nch; ch += 2) {
+    stage(ch, sa, la, sb, lb);
+    if (ch + 1 < nch) stage(ch + 1, sb, lb, sa, la);
   }
 #pragma unroll
   for (int q = 0; q < QS; ++q) {
@@ -749,9 +940,9 @@ hipError_t launch_prefill_td(const PrefillArgs& a, int stride, hipStream_t s) {
     const int nb = (a.P + bq - 1) / bq;
     hipLaunchKernelGGL((attend_kernel<T, D, true>), dim3((unsigned)(nb * a.units)), block, 0, s, a, stride, nb);
   } else {
-    constexpr int bq = AttendTile<T, D, false>::BQ;
+    constexpr int bq = RowTile<T, D>::BQ;
     const int nb = (a.P + bq - 1) / bq;
-    hipLaunchKernelGGL((attend_kernel<T, D, false>), dim3((unsigned)(nb * a.units)), block, 0, s, a, stride, nb);
+    hipLaunchKernelGGL((rowstats_kernel<T, D>), dim3((unsigned)(nb * a.units)), block, 0, s, a, stride, nb);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
