@@ -12,14 +12,17 @@
 //
 // Three kernels:
 //   rowstats : per query row i, lse_i = m_i + log2(sum_j exp2(s_ij - m_i)) with
-//              s in the log2 domain, from S^T tiles on MFMA;
+//              s in the log2 domain, from S^T tiles on MFMA (attend replaces it
+//              when the prompt's attention output is requested);
 //   colsum   : c_j = sum_i exp2(s_ij - lse_i), recomputing the S tiles on MFMA;
-//              each wavefront owns 64 columns (32 for f32) and walks the query
-//              tiles in a fixed order, so the sums are deterministic without
-//              atomics;
+//              each wavefront owns 32 columns and walks the query rows in a
+//              fixed order, so the sums are deterministic without atomics;
 //   select   : per unit, radix select of the h largest c_j among the older
 //              positions, then the gather of the kept K/V rows into slots
 //              (quantized to E4M3 with per-row scales for an E4M3 cache).
+// The moving operand of both sweeps goes through LDS in chunks of 32 rows
+// shared by a block's four wavefronts; loads of the next chunk are in flight
+// while the current one is multiplied.
 //
 // MFMA use: v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (f32).
 // Lane l supplies row l % 16 of a 16-row tile and the contiguous quarter
@@ -134,10 +137,9 @@ constexpr int rows_per_wave() { return kFixed<T> * kTile; }
 // probabilities of a chunk enter one MFMA.  The maximum is raised only when a
 // chunk exceeds it by more than kLazy (log2 units): unnormalised probabilities
 // stay below 2^kLazy and most chunks need no rescale of the accumulators.
-template <typename T, int D, bool OUT>
+template <typename T, int D>
 struct AttendTile {
-  // fixed query subtiles per wavefront: the output accumulators limit it to 2
-  static constexpr int QS = OUT || sizeof(T) == 4 ? 2 : 4;
+  static constexpr int QS = 2;  // fixed query subtiles per wavefront (the output accumulators limit it)
   static constexpr int ROWS = QS * kTile;             // queries per wavefront
   static constexpr int BQ = kWaves * ROWS;            // queries per block
   static constexpr int KC = 2 * kTile;                // keys per chunk
@@ -147,7 +149,7 @@ struct AttendTile {
   static constexpr int PIECES = KC * ROWB / 16;       // 16-byte pieces of a K (or V) chunk
   static constexpr int PER_T = (PIECES + kWaves * 64 - 1) / (kWaves * 64);
   static constexpr int NDT = D / 16;                  // 16-wide output column tiles
-  static constexpr int BUF = KC * (KSTR + (OUT ? VSTR : 0));  // bytes of one K (+ V) chunk
+  static constexpr int BUF = KC * (KSTR + VSTR);      // bytes of one K + V chunk
   static constexpr int NBUF = 2 * BUF <= 60 * 1024 ? 2 : 1;
 };
 
@@ -169,12 +171,10 @@ __device__ inline void load_lds_frag(Frag<T, D>& f, const char* base, int row0, 
   for (int i = 0; i < Frag<T, D>::kChunks; ++i) f.c[i] = *reinterpret_cast<const uint4*>(p + 16 * i);
 }
 
-// OUT = false computes only lse (the row statistics): four query subtiles per
-// wavefront, K chunks only, and a running maximum per lane group, merged at the end.
-template <typename T, int D, bool OUT>
+template <typename T, int D>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void attend_kernel(
     PrefillArgs a, int stride, int nblk) {
-  using AT = AttendTile<T, D, OUT>;
+  using AT = AttendTile<T, D>;
   constexpr int QS = AT::QS;
   constexpr int NDT = AT::NDT;
   constexpr float kLow = -1.0e30f;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       const int key = min(ch * AT::KC + idx / (AT::ROWB / 16), kend - 1);
       const int c16 = idx % (AT::ROWB / 16);
       rk[u] = load16(Kb + (size_t)key * AT::ROWB + c16 * 16);
-      if constexpr (OUT) rv[u] = load16(Vb + (size_t)key * AT::ROWB + c16 * 16);
+      rv[u] = load16(Vb + (size_t)key * AT::ROWB + c16 * 16);
     }
   };
   auto stash = [&](int ch, int b) __attribute__((always_inline)) {
@@ -237,19 +237,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
         const bool tail = (ch + 1) * AT::KC > kend;
         const bool in = !tail || ch * AT::KC + row < kend;
         *reinterpret_cast<uint4*>(kl + row * AT::KSTR + c16 * 16) = tail ? zero_unless(in, rk[u]) : rk[u];
-        if constexpr (OUT)
-          *reinterpret_cast<uint4*>(vl + row * AT::VSTR + c16 * 16) = tail ? zero_unless(in, rv[u]) : rv[u];
+        *reinterpret_cast<uint4*>(vl + row * AT::VSTR + c16 * 16) = tail ? zero_unless(in, rv[u]) : rv[u];
       }
     }
   };
 
-  // mask_tag: 1 = the chunk reaches past the wavefront's first query, 0 = it
-  // does not, 2 = decide at run time.  Row statistics use two instantiations
-  // behind a uniform branch, keeping the mask code out of the common path; the
-  // output variant keeps one body (a second copy of the value product would
-  // not fit the register budget).
-  auto compute = [&](auto mask_tag, int ch, const char* kl, const char* vl) __attribute__((always_inline)) {
-    constexpr int MASK = decltype(mask_tag)::value;
+  // One body for masked and unmasked chunks: a second copy of the value
+  // product (as the row statistics use) would not fit the register budget.
+  auto compute = [&](int ch, const char* kl, const char* vl) __attribute__((always_inline)) {
     const int c0 = ch * AT::KC;
     f32x4 s[2][QS];
 #pragma unroll
@@ -262,7 +257,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     // Causal mask.  Keys past P follow every query row < P; rows past P are not
     // written, so the causal test alone suffices.  Key 16*sub + 4g + i of the
     // chunk is kept for query qi iff 16*sub + i <= qi - c0 - 4g.
-    if (MASK == 1 || (MASK == 2 && c0 + AT::KC - 1 > qw0)) {
+    if (c0 + AT::KC - 1 > qw0) {  // uniform
 #pragma unroll
       for (int q = 0; q < QS; ++q) {
         const int t = qw0 + q * kTile + (lane & 15) - c0 - 4 * g;
@@ -281,10 +276,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       mx = fmaxf(fmaxf(mx, s[0][q][2]), s[0][q][3]);
       mx = fmaxf(fmaxf(mx, s[1][q][0]), s[1][q][1]);
       mx = fmaxf(fmaxf(mx, s[1][q][2]), s[1][q][3]);
-      if constexpr (OUT) {  // one maximum for the four lane groups of a query
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      }
+      // one maximum for the four lane groups of a query
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float ms = mx * sc;
       const bool raise = ms > m[q] + kLazy;
       const float mn = raise ? ms : m[q];
@@ -300,7 +294,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
                         ((p[1][q][0] + p[1][q][1]) + (p[1][q][2] + p[1][q][3]));
       l[q] = fmaf(l[q], alpha[q], add);
     }
-    if constexpr (!OUT) return;
     if (__any(raise_any)) {
 #pragma unroll
       for (int q = 0; q < QS; ++q)
@@ -348,14 +341,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   for (int ch = 0; ch < nch; ++ch) {
     if (ch + 1 < nch) fetch(ch + 1);
     const char* kl = smem + (ch % AT::NBUF) * AT::BUF;
-    if (ch * AT::KC <= qw_last) {  // uniform
-      if constexpr (OUT)
-        compute(std::integral_constant<int, 2>{}, ch, kl, kl + AT::KC * AT::KSTR);
-      else if (ch * AT::KC + AT::KC - 1 > qw0)
-        compute(std::integral_constant<int, 1>{}, ch, kl, kl + AT::KC * AT::KSTR);
-      else
-        compute(std::integral_constant<int, 0>{}, ch, kl, kl + AT::KC * AT::KSTR);
-    }
+    if (ch * AT::KC <= qw_last) compute(ch, kl, kl + AT::KC * AT::KSTR);  // uniform
     if (AT::NBUF == 1) __syncthreads();
     if (ch + 1 < nch) stash(ch + 1, (ch + 1) % AT::NBUF);
     __syncthreads();
@@ -365,23 +351,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
   for (int q = 0; q < QS; ++q) {
     float lt = l[q];
-    if constexpr (OUT) {
-      lt += __shfl_xor(lt, 16, 64);
-      lt += __shfl_xor(lt, 32, 64);
-    } else {  // merge the lane groups' (max, sum)
-#pragma unroll
-      for (int off = 16; off <= 32; off <<= 1) {
-        const float mo = __shfl_xor(m[q], off, 64);
-        const float lo = __shfl_xor(lt, off, 64);
-        const float mn = fmaxf(m[q], mo);
-        lt = lt * fast_exp2(m[q] - mn) + lo * fast_exp2(mo - mn);
-        m[q] = mn;
-      }
-    }
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
     const int qi = qw0 + q * kTile + (lane & 15);
-    if (!OUT && qi < P) {
-      if (g == 0) a.row_lse[(size_t)unit * stride + qi] = m[q] + __log2f(lt);
-    } else if (qi < P) {
+    if (qi < P) {
       const float inv = 1.f / lt;
       float* orow = a.out + ((size_t)unit * P + qi) * D + 4 * g;
 #pragma unroll
@@ -936,9 +909,9 @@ template <typename T, typename C, int D>
 hipError_t launch_prefill_td(const PrefillArgs& a, int stride, hipStream_t s) {
   const dim3 block(kWaves * 64);
   if (a.out) {
-    constexpr int bq = AttendTile<T, D, true>::BQ;
+    constexpr int bq = AttendTile<T, D>::BQ;
     const int nb = (a.P + bq - 1) / bq;
-    hipLaunchKernelGGL((attend_kernel<T, D, true>), dim3((unsigned)(nb * a.units)), block, 0, s, a, stride, nb);
+    hipLaunchKernelGGL((attend_kernel<T, D>), dim3((unsigned)(nb * a.units)), block, 0, s, a, stride, nb);
   } else {
     constexpr int bq = RowTile<T, D>::BQ;
     const int nb = (a.P + bq - 1) / bq;
