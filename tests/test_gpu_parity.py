@@ -422,3 +422,15 @@ def test_policy_e4m3_cache_and_prompt_output(policy):
     wl = WORKLOADS["opt6.7b"]
     run_workload(wl, 6, 64, kv_every=8, cache="e4m3", prompt_output=True, policy=policy)
     run_workload(heavy_only(wl, 250), 6, 64, kv_every=8, cache="e4m3", policy=policy)
+
+
+# ---- maximum budget -----------------------------------------------------------------------
+
+@pytest.mark.parametrize("cache_kind,split", [("input", 1), ("e4m3", 1), ("input", 3)])
+def test_maximum_budget(cache_kind, split):
+    """k = 8192 (the largest budget the C ABI accepts), prompt longer than k:
+    8192 + 1 logits in LDS, the E4M3 case with fewer wavefronts chosen by the
+    LDS check, and the split decode."""
+    wl = Workload(109, "max_budget_bf16", 1, 2, 128, 8300, 6, 4096, 4096, "bf16", "zipf", zipf_alpha=1.1)
+    assert wl.k == 8192
+    run_workload(wl, 2, 6, kv_every=3, cache=cache_kind, decode_split=split)
