@@ -106,6 +106,9 @@ typedef enum { H2O_POLICY_H2O = 0, H2O_POLICY_STATIC = 1, H2O_POLICY_NAIVE = 2 }
  * Results are bit-identical in every mode. */
 typedef enum { H2O_STEPS_AUTO = 0, H2O_STEPS_PER_STEP = 1, H2O_STEPS_PERSISTENT = 2 } h2o_steps_mode;
 
+/* Longest prompt a ctx can be created for (max_prompt). */
+#define H2O_MAX_PROMPT (1 << 28)
+
 /* Largest budget k = recent + heavy the decode kernel accepts (its per-row
  * logits live in LDS). */
 #define H2O_MAX_K 8192
@@ -116,7 +119,8 @@ typedef struct {
   int32_t head_dim;    /* 64, 96 or 128 */
   int32_t recent;      /* r >= 0: size of the protected window (includes the decoded token) */
   int32_t heavy;       /* h >= 0: heavy-hitter slots; 1 <= k = r + h <= H2O_MAX_K */
-  int32_t max_prompt;  /* >= 0: longest prompt h2o_prefill will accept (sizes the scratch) */
+  int32_t max_prompt;  /* 0 <= max_prompt <= H2O_MAX_PROMPT: longest prompt h2o_prefill will accept
+                          (sizes the scratch) */
   int32_t kv_dtype;    /* h2o_dtype of q, k, v inputs and of the K/V slots */
   float scale;         /* softmax scale; 0 selects 1/sqrt(head_dim) */
   int32_t start_pos;   /* adopt an existing state: position of the next token to decode */

@@ -19,6 +19,7 @@ POLICIES = {"h2o": H2O_POLICY_H2O, "static": H2O_POLICY_STATIC, "naive": H2O_POL
 H2O_STEPS_AUTO, H2O_STEPS_PER_STEP, H2O_STEPS_PERSISTENT = 0, 1, 2
 STEPS_MODES = {"auto": H2O_STEPS_AUTO, "per_step": H2O_STEPS_PER_STEP, "persistent": H2O_STEPS_PERSISTENT}
 H2O_MAX_K = 8192
+H2O_MAX_PROMPT = 1 << 28
 
 STATUS_NAMES = {
     H2O_OK: "H2O_OK",

@@ -37,7 +37,8 @@ bool valid_dims(const h2o_config* c) {
          (c->policy == H2O_POLICY_H2O || c->policy == H2O_POLICY_STATIC || c->policy == H2O_POLICY_NAIVE) &&
          (c->steps_mode == H2O_STEPS_AUTO || c->steps_mode == H2O_STEPS_PER_STEP ||
           c->steps_mode == H2O_STEPS_PERSISTENT) &&
-         c->max_prompt >= 0 && (c->kv_dtype == H2O_F32 || c->kv_dtype == H2O_BF16) &&
+         c->max_prompt >= 0 && c->max_prompt <= H2O_MAX_PROMPT &&
+         (c->kv_dtype == H2O_F32 || c->kv_dtype == H2O_BF16) &&
          isfinite(c->scale) && c->scale >= 0.f && c->start_pos >= 0 && c->start_live >= 0 &&
          (c->decode_waves == 0 || c->decode_waves == 1 || c->decode_waves == 2 ||
           c->decode_waves == 4 || c->decode_waves == 8) &&
@@ -105,7 +106,7 @@ h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** o
   c->t = t0;
   c->n_live = n0;
   c->has_state = n0 > 0;
-  c->stride = (cfg->max_prompt + 15) / 16 * 16;
+  c->stride = (int32_t)(((int64_t)cfg->max_prompt + 15) / 16 * 16);
   c->scratch = nullptr;
   c->split_mem = nullptr;
   c->split = h2o::SplitScratch{nullptr, nullptr, nullptr, 1};

@@ -60,7 +60,7 @@ int main(void) {
          offsetof(h2o_config, decode_split), offsetof(h2o_config, cache_dtype),
          offsetof(h2o_state, v_scale), offsetof(h2o_config, policy), offsetof(h2o_config, steps_mode));
   printf("%d %d %d\n", H2O_POLICY_H2O, H2O_POLICY_STATIC, H2O_POLICY_NAIVE);
-  printf("%d\n", H2O_MAX_K);
+  printf("%d %d\n", H2O_MAX_K, H2O_MAX_PROMPT);
   return 0;
 }''')
     exe = tmp_path / "layout"
@@ -74,7 +74,7 @@ int main(void) {
                    B.h2o_config.policy.offset, B.h2o_config.steps_mode.offset]
     assert list(map(int, lines[1].split())) == [B.H2O_POLICY_H2O, B.H2O_POLICY_STATIC,
                                                 B.H2O_POLICY_NAIVE]
-    assert int(lines[2]) == B.H2O_MAX_K
+    assert list(map(int, lines[2].split())) == [B.H2O_MAX_K, B.H2O_MAX_PROMPT]
 
 
 def test_status_strings():
@@ -93,6 +93,8 @@ def test_status_strings():
     (dict(steps_mode=3), B.H2O_ERR_INVALID),
     (dict(heavy=-1), B.H2O_ERR_INVALID),
     (dict(max_prompt=-5), B.H2O_ERR_INVALID),
+    (dict(max_prompt=(1 << 28) + 1), B.H2O_ERR_INVALID),
+    (dict(max_prompt=INT32_MAX), B.H2O_ERR_INVALID),
     (dict(kv_dtype=7), B.H2O_ERR_INVALID),
     (dict(scale=-1.0), B.H2O_ERR_INVALID),
     (dict(scale=float("nan")), B.H2O_ERR_INVALID),
