@@ -88,10 +88,13 @@ def _oracle_worker(args):
     wl = dc.replace(W[wl_name], recent=recent, heavy=heavy)
     with threadpool_limits(1):
         data = []
+        pre_s = 0.0
         for u in units:
             b, h = divmod(u, wl.heads)
             Q, K, V = gen.unit_values(wl, b, h, 0, wl.prompt + steps)
+            tp = time.perf_counter()
             m, _ = prefill(Q[:wl.prompt], K[:wl.prompt], wl.recent, wl.heavy, wl.scale, policy)
+            pre_s += time.perf_counter() - tp
             data.append((Q, K, V, m))
         t0 = time.perf_counter()
         for Q, K, V, m in data:
@@ -99,7 +102,7 @@ def _oracle_worker(args):
                 t = wl.prompt + s
                 m = decode_step(m, t, Q[t], K, V, wl.recent, wl.heavy, wl.scale, policy=policy).members
         dt = time.perf_counter() - t0
-    return len(units) * steps, dt
+    return len(units) * steps, dt, len(units), pre_s
 
 
 def cpu_baseline(wl, units_per_worker, steps, policy="h2o"):
@@ -111,8 +114,10 @@ def cpu_baseline(wl, units_per_worker, steps, policy="h2o"):
     jobs = [j for j in jobs if j[4]]
     with mp.get_context("fork").Pool(len(jobs)) as pool:
         res = pool.map(_oracle_worker, jobs)
-    unit_steps_per_s = sum(n / dt for n, dt in res)
-    cpu_work = sum(dt for _, dt in res)
+    unit_steps_per_s = sum(n / dt for n, dt, _, _ in res)
+    cpu_work = sum(dt for _, dt, _, _ in res)
+    # oracle prefill: per-unit time on one core, scaled to the whole batch over the workers
+    pre_unit_s = sum(ps for _, _, _, ps in res) / sum(nu for _, _, nu, _ in res)
     model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -126,6 +131,7 @@ def cpu_baseline(wl, units_per_worker, steps, policy="h2o"):
         "unit": "steps/s",
         "cores": len(jobs),
         "kind": "oracle",
+        "prefill_s": pre_unit_s * wl.units / len(jobs),
         "sample": (f"{len(chosen)} of {wl.units} (batch, head) units x {steps} decode steps "
                    f"after an untimed oracle prefill, float64 numpy, {len(jobs)} processes with one "
                    f"BLAS thread each; {cpu_work:.1f} s of CPU time; rate scaled to whole-batch "
@@ -217,6 +223,22 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
         stream_ms = r0.elapsed_time(r1)
         pc.close()
     del prompt_keep
+    copy_gbs = None
+    if not copy_mib:
+        # device-to-device copy of 2 GiB, as a measured ceiling for context (left out of
+        # counter runs, whose copies calibrate the byte counters)
+        xc = torch.empty(1 << 30, dtype=torch.int16, device=dev)
+        yc = torch.empty_like(xc)
+        xc.fill_(1)
+        yc.copy_(xc)
+        torch.cuda.synchronize()
+        r0.record(stream)
+        for _ in range(5):
+            yc.copy_(xc)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbs = 5 * 2 * xc.numel() * 2 / (r0.elapsed_time(r1) * 1e-3) / 1e9
+        del xc, yc
     if copy_mib:
         # plain device copy of known size, for scaling the HBM byte counters
         x = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -230,9 +252,15 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     if waves == 0:
         waves_used = decode_waves_auto(wl.units)
     cache.close()
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", ""),
+              "compute_units": props.multi_processor_count,
+              "memory_gib": round(props.total_memory / 2 ** 30, 1)}
+    clock = getattr(props, "clock_rate", None)
+    if clock:
+        device["clock_mhz"] = clock / 1000
     return dict(region_ms=region_ms, stream_ms=stream_ms, prefill_ms=prefill_ms, prefill_out_ms=prefill_out_ms,
-                waves=waves_used,
-                device=torch.cuda.get_device_name(0))
+                waves=waves_used, device=device, copy_gbs=copy_gbs)
 
 
 def decode_waves_auto(units):
@@ -340,6 +368,8 @@ def main():
             "ms": g["prefill_ms"],
             "qk_tflops": prefill_flops(wl) / (g["prefill_ms"] * 1e-3) / 1e12,
             "peak_tflops": PEAK_BF16_TFLOPS if wl.kv_dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS,
+            "frac": prefill_flops(wl) / (g["prefill_ms"] * 1e-3) / 1e12 /
+                    (PEAK_BF16_TFLOPS if wl.kv_dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS),
             "with_output": {
                 "ms": g["prefill_out_ms"],
                 # causal QK^T and PV: each P(P+1)/2 dot products of length d per unit
@@ -357,6 +387,9 @@ def main():
             "achieved": bytes_step * steps / (g["stream_ms"] * 1e-3) / 1e9,
             "frac": bytes_step * steps / (g["stream_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         },
+        "copy_ceiling": None if g["copy_gbs"] is None else {
+            "kind": "device-to-device copy, 2 GiB read + 2 GiB written (torch)",
+            "GBps": g["copy_gbs"], "frac": g["copy_gbs"] / PEAK_HBM_GBS},
         "cpu_baseline": cpu,
         "device": g["device"],
     }
