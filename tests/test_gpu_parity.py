@@ -53,6 +53,39 @@ def run_workload(wl, n_units, steps, check_every=1, decode_waves=0, kv_every=64,
     return stats
 
 
+# ---- free-running trajectories of the ablation policies -----------------------------
+
+def test_policies_free_running_match_recorded_trajectories():
+    """The GPU alone runs the tiny workload under each recorded policy and budget;
+    its evictions equal the oracle's own trajectory up to the first step whose
+    two lowest candidates are closer than 1e-5 (naive per-step Top-K compares
+    single weights, which come close), and all of it where there is none."""
+    from kv_cache_eviction_02_amd import H2OCache
+    wl = WORKLOADS["tiny_fp32"]
+    rec = json.load(open(os.path.join(HERE, "golden", "tiny_fp32_policy_traces.json")))
+    dq, dk, dv = stage_decode(wl, 0, wl.steps, "cuda")
+    for case in rec["cases"]:
+        cache = H2OCache(wl.batch, wl.heads, wl.head_dim, case["recent"], case["heavy"], wl.prompt,
+                         torch.float32, wl.scale, policy=case["policy"])
+        cache.prefill(*stage_prompt(wl, "cuda"))
+        evs = []
+        for s in range(wl.steps):
+            _, ev = cache.step(dq[s], dk[s], dv[s])
+            evs.append(ev.view(-1).cpu().numpy().copy())
+        evs = np.array(evs)
+        for u in case["units"]:
+            gaps = u["min_gap"]
+            upto = next((i for i, g in enumerate(gaps) if g is not None and g < 1e-5), len(gaps))
+            say(f"[parity] {case['policy']} r={case['recent']} h={case['heavy']} head {u['head']}: "
+                f"{upto} of {len(gaps)} steps before a near-tie")
+            assert evs[:upto, u["head"]].tolist() == u["evicted"][:upto], case["policy"]
+            if upto == len(gaps):
+                got = sorted(cache.pos.view(wl.units, -1)[u["head"]].cpu().tolist())
+                got = [p for p in got if p >= 0]
+                assert got == u["final_members"]
+        cache.close()
+
+
 # ---- the five workloads --------------------------------------------------------
 
 def test_tiny_fp32_every_step():

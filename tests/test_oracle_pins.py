@@ -553,3 +553,18 @@ def test_naive_policy_forgets_accumulated_mass():
     w /= w.sum()
     for j in (1, 2):
         assert naive.members[j] == pytest.approx(w[j], rel=1e-13)
+
+
+def test_policy_traces_match_recorded_trajectories():
+    # regression record of the oracle's ablation policies (tests/golden/make_policy_traces.py)
+    import json
+    import os
+    rec = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tiny_fp32_policy_traces.json")))
+    for case in rec["cases"]:
+        for u in case["units"]:
+            wl, Q, K, V = c1_unit(u["head"])
+            seeded, _, steps = run_trace(Q, K, V, wl.prompt, wl.steps, case["recent"], case["heavy"], wl.scale,
+                                         policy=case["policy"])
+            assert sorted(seeded) == u["prefill_kept"], case["policy"]
+            assert [s.evicted for s in steps] == u["evicted"], case["policy"]
+            assert sorted(steps[-1].members) == u["final_members"], case["policy"]
