@@ -15,7 +15,7 @@
 // replaces each score by the current weight instead of adding it, and r = 0
 // (heavy-only) makes the decoded token itself a candidate.
 //
-// Two kernels share the streaming loop and the final score/eviction code:
+// Three kernels share the streaming loop and the final score/eviction code:
 //
 // decode_kernel: one workgroup per (batch, head) unit.  K and V rows are
 //   streamed once with 16-byte non-temporal loads, a row spread over
@@ -36,6 +36,10 @@
 //   unit's arrival counter; the last to arrive combines the partials, runs the
 //   score update and eviction, and resets the counter.  No workgroup waits for
 //   another.
+//
+// decode_multi_kernel: n steps over tokens known in advance in one launch; each
+//   workgroup carries its unit from step to step with the scores and positions
+//   in LDS, so one unit's end-of-step work overlaps the others' streaming.
 //
 // E4M3 cache (C = e4m3, bf16 inputs): slots hold E4M3 codes with one float32
 // scale per row; the K scale multiplies the row's logit and the V scale its
