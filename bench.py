@@ -56,11 +56,20 @@ def prefill_flops(wl):
     return wl.units * P * (P + 1) * wl.head_dim
 
 
+def code_text(src):
+    """Source text without comments and whitespace: what the compiler sees."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def decode_source_hash():
+    """Hash of the decode sources' code (comments and layout ignored)."""
     h = hashlib.sha256()
     for rel in DECODE_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 
