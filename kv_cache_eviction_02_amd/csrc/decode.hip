@@ -88,6 +88,7 @@ struct Geo {
   static_assert(!kQuant || std::is_same<T, bf16>::value, "E4M3 cache takes bf16 inputs");
 };
 
+constexpr float kLazyMax = 8.f;  // log2 units a row group's running maximum may lag
 constexpr int kSelfVictim = -2;  // victim marker: the decoded token itself (r = 0)
 
 // One unit's step as seen by every thread.  With r = 0 there is no ring:
@@ -204,16 +205,20 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
           }
         }
       }
-      const float mn = fmaxf(m, lg);
-      if (mn > -INFINITY) {
-        const float alpha = fast_exp2(m - mn);
-        const float p = fast_exp2(lg - mn);  // 0 for rows outside the range
+      if (lg > m + kLazyMax) {  // rare after the first rows: rescale to the new maximum
+        const float alpha = fast_exp2(m - lg);  // 0 while m is -inf
+        lsum *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] *= alpha;
+        m = lg;
+      }
+      if (m > -INFINITY) {
+        const float p = fast_exp2(lg - m);  // 0 for rows outside the range; at most 2^kLazyMax
         float vf[EPL];
         EC::unpack(vr, vf);
-        lsum = fmaf(lsum, alpha, p);
+        lsum += p;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vf[e], o[e] * alpha);
-        m = mn;
+        for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vf[e], o[e]);
       }
     };
     uint4 ka, va, kb, vb;
@@ -277,17 +282,21 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
           }
         }
       }
-      const float mn = fmaxf(m, lg);
-      if (mn > -INFINITY) {
-        const float alpha = fast_exp2(m - mn);
-        const float p = fast_exp2(lg - mn);
+      if (lg > m + kLazyMax) {  // rare after the first rows: rescale to the new maximum
+        const float alpha = fast_exp2(m - lg);  // 0 while m is -inf
+        lsum *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] *= alpha;
+        m = lg;
+      }
+      if (m > -INFINITY) {
+        const float p = fast_exp2(lg - m);
         const float pv = p * vsc;
         float vf[EPL];
         EC::unpack(vr, vf);
-        lsum = fmaf(lsum, alpha, p);
+        lsum += p;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = fmaf(pv, vf[e], o[e] * alpha);
-        m = mn;
+        for (int e = 0; e < EPL; ++e) o[e] = fmaf(pv, vf[e], o[e]);
       }
     };
     uint4 ka, va, kb, vb;
