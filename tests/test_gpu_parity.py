@@ -293,7 +293,7 @@ def test_run_twice_bitwise_identical():
                            b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
 
 
-def _steps_vs_single(wl, n, split_at, cache_kind="input", policy="h2o", decode_waves=0):
+def _steps_vs_single(wl, n, split_at, cache_kind="input", policy="h2o", decode_waves=0, decode_split=1):
     """Run n steps as single h2o_decode_step calls and as h2o_decode_steps calls
     (split at split_at); return both runs' outputs, evictions and final state."""
     from kv_cache_eviction_02_amd import H2OCache
@@ -303,7 +303,7 @@ def _steps_vs_single(wl, n, split_at, cache_kind="input", policy="h2o", decode_w
     res = []
     for multi in (False, True):
         cache = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy, wl.prompt, dtype, wl.scale,
-                         cache=cache_kind, policy=policy, decode_waves=decode_waves,
+                         cache=cache_kind, policy=policy, decode_waves=decode_waves, decode_split=decode_split,
                          steps_mode="persistent" if multi else "per_step")
         cache.prefill(*prompt)
         if multi:
@@ -334,6 +334,8 @@ def _steps_vs_single(wl, n, split_at, cache_kind="input", policy="h2o", decode_w
 
 STEPS_CASES = [  # (workload, n, split point, cache, policy, waves)
     ("opt6.7b", 96, 40, "input", "h2o", 0),
+    # decode split over 4 workgroups: h2o_decode_steps falls back to one launch per step
+    ("llama7b_stream", 48, 20, "input", "h2o", -4),
     ("llama7b_stream", 96, 40, "input", "h2o", 0),
     ("opt30b", 24, 7, "input", "h2o", 0),
     ("opt30b", 24, 7, "e4m3", "h2o", 0),
@@ -348,7 +350,8 @@ def test_decode_steps_equals_single_steps(name, n, split_at, cache_kind, policy,
     """h2o_decode_steps (one persistent launch per call) gives bit-identical
     outputs, evictions and state to the same steps as h2o_decode_step calls."""
     say(f"[parity] decode_steps vs decode_step: {name}, {n} steps, {cache_kind}, {policy}")
-    a, b = _steps_vs_single(WORKLOADS[name], n, split_at, cache_kind, policy, waves)
+    split = -waves if waves < 0 else 1
+    a, b = _steps_vs_single(WORKLOADS[name], n, split_at, cache_kind, policy, max(waves, 0), split)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 
