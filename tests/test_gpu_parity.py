@@ -332,26 +332,25 @@ def _steps_vs_single(wl, n, split_at, cache_kind="input", policy="h2o", decode_w
     return res
 
 
-STEPS_CASES = [  # (workload, n, split point, cache, policy, waves)
-    ("opt6.7b", 96, 40, "input", "h2o", 0),
+STEPS_CASES = [  # (workload, n, split point, cache, policy, waves, decode split)
+    ("opt6.7b", 96, 40, "input", "h2o", 0, 1),
     # decode split over 4 workgroups: h2o_decode_steps falls back to one launch per step
-    ("llama7b_stream", 48, 20, "input", "h2o", -4),
-    ("llama7b_stream", 96, 40, "input", "h2o", 0),
-    ("opt30b", 24, 7, "input", "h2o", 0),
-    ("opt30b", 24, 7, "e4m3", "h2o", 0),
-    ("opt6.7b", 64, 1, "e4m3", "naive", 2),
-    ("tiny_fp32", 64, 30, "input", "static", 1),
-    ("neox20b", 12, 5, "input", "h2o", 0),
+    ("llama7b_stream", 48, 20, "input", "h2o", 0, 4),
+    ("llama7b_stream", 96, 40, "input", "h2o", 0, 1),
+    ("opt30b", 24, 7, "input", "h2o", 0, 1),
+    ("opt30b", 24, 7, "e4m3", "h2o", 0, 1),
+    ("opt6.7b", 64, 1, "e4m3", "naive", 2, 1),
+    ("tiny_fp32", 64, 30, "input", "static", 1, 1),
+    ("neox20b", 12, 5, "input", "h2o", 0, 1),
 ]
 
 
-@pytest.mark.parametrize("name,n,split_at,cache_kind,policy,waves", STEPS_CASES)
-def test_decode_steps_equals_single_steps(name, n, split_at, cache_kind, policy, waves):
+@pytest.mark.parametrize("name,n,split_at,cache_kind,policy,waves,split", STEPS_CASES)
+def test_decode_steps_equals_single_steps(name, n, split_at, cache_kind, policy, waves, split):
     """h2o_decode_steps (one persistent launch per call) gives bit-identical
     outputs, evictions and state to the same steps as h2o_decode_step calls."""
-    say(f"[parity] decode_steps vs decode_step: {name}, {n} steps, {cache_kind}, {policy}")
-    split = -waves if waves < 0 else 1
-    a, b = _steps_vs_single(WORKLOADS[name], n, split_at, cache_kind, policy, max(waves, 0), split)
+    say(f"[parity] decode_steps vs decode_step: {name}, {n} steps, {cache_kind}, {policy}, split {split}")
+    a, b = _steps_vs_single(WORKLOADS[name], n, split_at, cache_kind, policy, waves, split)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 
