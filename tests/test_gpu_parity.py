@@ -469,3 +469,42 @@ def test_maximum_budget(cache_kind, split):
     wl = Workload(109, "max_budget_bf16", 1, 2, 128, 8300, 6, 4096, 4096, "bf16", "zipf", zipf_alpha=1.1)
     assert wl.k == 8192
     run_workload(wl, 2, 6, kv_every=3, cache=cache_kind, decode_split=split)
+
+
+# ---- seeded random configurations ---------------------------------------------------------
+
+def _random_cases(n=48, seed=2024):
+    """Small random configurations mixing every option the C ABI takes: head
+    dimension, input dtype, cache format, window and heavy sizes (either may be
+    zero), prompt and step counts down to one, policy, split decode and the
+    prompt output.  Each one is checked against the oracle at every step."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 96, 128]))
+        kv = "f32" if rng.random() < 0.3 else "bf16"
+        cache = "e4m3" if kv == "bf16" and rng.random() < 0.35 else "input"
+        recent = int(rng.choice([0, 1, 2, 5, 8, 16, 33]))
+        heavy = int(rng.choice([0, 1, 3, 7, 16, 40]))
+        if recent + heavy == 0:
+            heavy = 2
+        prompt = int(rng.choice([1, 2, 7, 16, 31, 64, 97]))
+        steps = int(rng.choice([1, 3, 17, 40]))
+        skew = str(rng.choice(["fraction", "zipf", "bursts"]))
+        wl = Workload(300 + i, f"rand{i:02d}", int(rng.integers(1, 3)), int(rng.integers(1, 4)), d,
+                      prompt, steps, recent, heavy, kv, skew, skew_frac=0.1, zipf_alpha=1.1,
+                      burst_len=4)
+        policy = str(rng.choice(["h2o", "h2o", "static", "naive"]))
+        split = int(rng.choice([1, 1, 2, 5]))
+        waves = int(rng.choice([0, 1, 2, 4]))
+        output = bool(rng.random() < 0.3)
+        cases.append((wl, cache, policy, split, waves, output))
+    return cases
+
+
+@pytest.mark.parametrize("wl,cache,policy,split,waves,output", _random_cases(),
+                         ids=lambda v: v.name if isinstance(v, Workload) else None)
+def test_random_configurations(wl, cache, policy, split, waves, output):
+    stats = run_workload(wl, wl.units, wl.steps, kv_every=1, decode_split=split, decode_waves=waves,
+                         cache=cache, prompt_output=output, policy=policy)
+    assert stats.steps == wl.steps
