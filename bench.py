@@ -89,12 +89,12 @@ def traffic_for(wl_name, waves, cache="input"):
 # ---- CPU baseline: the oracle on the host cores (runs before any GPU use) -------
 
 def _oracle_worker(args):
-    wl_name, recent, heavy, policy, units, steps = args
+    wl_name, prompt, recent, heavy, policy, units, steps = args
     import dataclasses as dc
     from threadpoolctl import threadpool_limits
     from oracle import decode_step, prefill
     from synth import WORKLOADS as W, gen
-    wl = dc.replace(W[wl_name], recent=recent, heavy=heavy)
+    wl = dc.replace(W[wl_name], prompt=prompt, recent=recent, heavy=heavy)
     with threadpool_limits(1):
         data = []
         pre_s = 0.0
@@ -119,8 +119,9 @@ def cpu_baseline(wl, units_per_worker, steps, policy="h2o"):
     workers = min(16, len(os.sched_getaffinity(0)))
     stride = max(1, wl.units // (workers * units_per_worker))
     chosen = list(range(0, wl.units, stride))[:workers * units_per_worker]
-    jobs = [(wl.name, wl.recent, wl.heavy, policy, chosen[i::workers], steps) for i in range(workers)]
-    jobs = [j for j in jobs if j[4]]
+    jobs = [(wl.name, wl.prompt, wl.recent, wl.heavy, policy, chosen[i::workers], steps)
+            for i in range(workers)]
+    jobs = [j for j in jobs if j[5]]
     with mp.get_context("fork").Pool(len(jobs)) as pool:
         res = pool.map(_oracle_worker, jobs)
     unit_steps_per_s = sum(n / dt for n, dt, _, _ in res)
@@ -257,9 +258,7 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
             y.copy_(x)
         torch.cuda.synchronize()
         del x, y
-    waves_used = waves
-    if waves == 0:
-        waves_used = decode_waves_auto(wl.units)
+    waves_used, split_used = cache.launch_shape()
     cache.close()
     props = torch.cuda.get_device_properties(0)
     device = {"name": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", ""),
@@ -269,15 +268,7 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     if clock:
         device["clock_mhz"] = clock / 1000
     return dict(region_ms=region_ms, stream_ms=stream_ms, prefill_ms=prefill_ms, prefill_out_ms=prefill_out_ms,
-                waves=waves_used, device=device, copy_gbs=copy_gbs)
-
-
-def decode_waves_auto(units):
-    # mirrors the library's automatic choice, for reporting only
-    w = 1
-    while w < 8 and units * w * 2 <= 4096:
-        w *= 2
-    return w
+                waves=waves_used, split=split_used, device=device, copy_gbs=copy_gbs)
 
 
 def main():
@@ -293,6 +284,9 @@ def main():
                     help="eviction policy: H2O or one of its ablations")
     ap.add_argument("--heavy-only", action="store_true",
                     help="no protected window: recent = 0, heavy = the workload's k")
+    ap.add_argument("--prompt", type=int, default=0, help="override the workload's prompt length")
+    ap.add_argument("--budget", default="",
+                    help="override the workload's budget as RECENT,HEAVY (e.g. a long context)")
     ap.add_argument("--decode-split", type=int, default=0,
                     help="decode workgroups per (batch, head) unit; 0 = library default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -312,8 +306,14 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     wl = WORKLOADS[args.workload]
+    if args.prompt:
+        wl = dataclasses.replace(wl, prompt=args.prompt)
+    if args.budget:
+        r, h = (int(x) for x in args.budget.split(","))
+        wl = dataclasses.replace(wl, recent=r, heavy=h)
     if args.heavy_only:
         wl = dataclasses.replace(wl, recent=0, heavy=wl.k)
+    modified = bool(args.prompt or args.budget or args.heavy_only)
     steps = args.steps
     warmup = args.warmup
     if warmup + steps > wl.steps:
@@ -337,7 +337,7 @@ def main():
     bytes_step = alg_bytes_per_step(wl, args.cache)
     achieved = bytes_step / (mean_launch_ms * 1e-3) / 1e9
     traffic = traffic_for(wl.name, g["waves"], args.cache) \
-        if args.policy == "h2o" and not args.heavy_only else None
+        if args.policy == "h2o" and not modified and g["split"] == 1 else None
     line = {
         "metric": METRIC,
         "value": 1e3 / ms_per_step,
@@ -356,7 +356,8 @@ def main():
             "prompt": wl.prompt, "k": wl.k, "recent": wl.recent, "heavy": wl.heavy,
             "kv_dtype": wl.kv_dtype, "cache": args.cache, "policy": args.policy,
             "decode_waves": g["waves"],
-            "decode_split": args.decode_split or "auto",
+            "decode_split": g["split"],
+            "launch_shape": "explicit" if args.decode_waves or args.decode_split else "automatic",
             "parallelism": "none",
             "launch": ("h2o_decode_step per step" if args.single_step_calls
                        else "h2o_decode_steps, one launch per step"),
@@ -369,7 +370,7 @@ def main():
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "kernel": "decode_kernel",
+            "kernel": "decode_kernel" if g["split"] == 1 else "decode_split_kernel",
             "alg_bytes_per_launch": bytes_step,
             "mean_launch_us": mean_launch_ms * 1e3,
         },

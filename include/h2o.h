@@ -127,8 +127,10 @@ typedef struct {
   int32_t start_live;  /* adopt an existing state: number of live slots (0 = no state yet) */
   int32_t decode_waves;/* wavefronts per decode workgroup: 0 = automatic, else 1, 2, 4 or 8 */
   int32_t decode_split;/* decode workgroups per (batch, head) unit: 0 = automatic, 1 = one,
-                          2..64 = that many (each streams a share of the rows; for batches
-                          with few units) */
+                          2..64 = that many (each streams a share of the rows).  Automatic
+                          splits only when the units are fewer than the device's compute
+                          units, the workgroups have 8 wavefronts and every share keeps at
+                          least 512 rows (long contexts at small batch) */
   int32_t cache_dtype; /* h2o_cache_dtype */
   int32_t policy;      /* h2o_policy */
   int32_t steps_mode;  /* h2o_steps_mode */
@@ -206,6 +208,11 @@ h2o_status h2o_decode_steps(h2o_ctx* ctx, int32_t n_steps, const void* q, const 
 /* Host-side counters: position of the next token to decode and number of live
  * slots per unit (the same for every unit).  Either pointer may be NULL. */
 h2o_status h2o_query(const h2o_ctx* ctx, int32_t* next_pos, int32_t* n_live);
+
+/* Decode launch shape chosen at h2o_create: wavefronts per workgroup and
+ * workgroups per (batch, head) unit (1 = no split), after the automatic
+ * choices and the LDS check.  Either pointer may be NULL. */
+h2o_status h2o_launch_shape(const h2o_ctx* ctx, int32_t* decode_waves, int32_t* decode_split);
 
 /* Free the scratch and the ctx.  NULL-safe.  Never frees caller buffers.  The
  * caller must make sure no enqueued work still uses the ctx's scratch. */

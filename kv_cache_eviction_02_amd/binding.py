@@ -93,6 +93,8 @@ def load_library(path=LIB_PATH):
     lib.h2o_decode_steps.restype = ctypes.c_int
     lib.h2o_query.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.h2o_query.restype = ctypes.c_int
+    lib.h2o_launch_shape.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.h2o_launch_shape.restype = ctypes.c_int
     lib.h2o_destroy.argtypes = [vp]
     lib.h2o_destroy.restype = ctypes.c_int
     lib.h2o_status_string.argtypes = [ctypes.c_int]
@@ -139,6 +141,12 @@ def h2o_query(ctx):
     t, n = ctypes.c_int32(), ctypes.c_int32()
     st = load_library().h2o_query(ctx, ctypes.byref(t), ctypes.byref(n))
     return st, t.value, n.value
+
+
+def h2o_launch_shape(ctx):
+    w, s = ctypes.c_int32(), ctypes.c_int32()
+    st = load_library().h2o_launch_shape(ctx, ctypes.byref(w), ctypes.byref(s))
+    return st, w.value, s.value
 
 
 def h2o_destroy(ctx):
@@ -279,6 +287,12 @@ class H2OCache:
         st, t, n = h2o_query(self.ctx)
         _check(st, "h2o_query")
         return t, n
+
+    def launch_shape(self):
+        """(wavefronts per decode workgroup, workgroups per unit) chosen at creation."""
+        st, w, sp = h2o_launch_shape(self.ctx)
+        _check(st, "h2o_launch_shape")
+        return w, sp
 
     def close(self):
         if getattr(self, "ctx", None):

@@ -623,6 +623,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 2
   }
 }
 
+// Device-scope (agent) relaxed store and load: global_store / global_load with
+// sc1 on gfx950, coherent across the XCDs without a cache writeback.
+__device__ __forceinline__ void publish(float* p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float collect(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <typename T, typename C, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, SplitScratch sp) {
   using GG = Geo<T, C, D, NW>;
@@ -670,32 +679,34 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   const GroupMerge<NG> gm = merge_groups<GG, D>(m, lsum, o, s_o, s_m, s_l);
 
   // This workgroup's partial: max, sum, output relative to its max; its logits.
+  // Device-scope stores (sc1): each is written through to the level that all
+  // XCDs share, so no cache of this XCD has to be written back for the
+  // combining workgroup (possibly on another XCD) to read it.
   float* pp = sp.partials + ((size_t)unit * S + part) * (D + 2);
   if (tid == 0) {
-    pp[0] = gm.M;
-    pp[1] = gm.L;
+    publish(pp + 0, gm.M);
+    publish(pp + 1, gm.L);
   }
   for (int c = tid; c < D; c += NT) {
     float acc = 0.f;
 #pragma unroll
     for (int g = 0; g < NG; ++g) acc = fmaf(s_o[g][c], gm.wg[g], acc);
-    pp[2 + c] = acc;
+    publish(pp + 2 + c, acc);
   }
   float* lg = sp.logits + (size_t)unit * (v.k + 1);
-  for (int j = lo + tid; j < hi; j += NT) lg[j] = s_logit[j];
+  for (int j = lo + tid; j < hi; j += NT) publish(lg + j, s_logit[j]);
 
-  // Publish, count arrivals; the last workgroup of the unit finishes the step.
-  // The workgroup barrier completes every thread's stores; one agent-scope
-  // release by thread 0 then makes them visible to the other XCDs before the
-  // arrival is counted (a device-scope fence writes back the XCD's L2, so it
-  // is issued once per workgroup, not once per thread).
+  // Count arrivals; the last workgroup of the unit finishes the step.  Every
+  // thread waits until its device-scope stores are acknowledged before the
+  // barrier, so when thread 0 counts the arrival all of the workgroup's
+  // partials are visible at device scope; the combining workgroup reads them
+  // with device-scope loads after it has seen the final count.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const unsigned prev = __hip_atomic_fetch_add(sp.counters + unit, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == (unsigned)(S - 1);
-    if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
   if (!s_last) return;
@@ -703,24 +714,24 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   // Combine the partials.
   const float* up = sp.partials + (size_t)unit * S * (D + 2);
   float M = -INFINITY;
-  for (int c = 0; c < S; ++c) M = fmaxf(M, up[(size_t)c * (D + 2)]);
+  for (int c = 0; c < S; ++c) M = fmaxf(M, collect(up + (size_t)c * (D + 2)));
   float L = 0.f;
   for (int c = 0; c < S; ++c) {
     const float* q = up + (size_t)c * (D + 2);
-    L = fmaf(q[1], fast_exp2(q[0] - M), L);
+    L = fmaf(collect(q + 1), fast_exp2(collect(q) - M), L);
   }
   const float invL = 1.f / L;
   for (int d = tid; d < D; d += NT) {
     float acc = 0.f;
     for (int c = 0; c < S; ++c) {
       const float* q = up + (size_t)c * (D + 2);
-      acc = fmaf(q[2 + d], fast_exp2(q[0] - M), acc);
+      acc = fmaf(collect(q + 2 + d), fast_exp2(collect(q) - M), acc);
     }
     a.out[(size_t)unit * D + d] = acc * invL;
   }
   // All logits, and the rows the admission writes (still intact: only this
   // workgroup writes the unit's state).
-  for (int j = tid; j < v.n_att; j += NT) s_logit[j] = lg[j];
+  for (int j = tid; j < v.n_att; j += NT) s_logit[j] = collect(lg + j);
   if (tid < LPR) {
     if constexpr (!GG::kQuant) {
       st.self[0][tid] = load16(u.kn + tid * 16);
@@ -815,13 +826,19 @@ int decode_waves_auto(int units) {
   return w;
 }
 
-int decode_split_auto(int units, int waves) {
-  // Measured on MI355X: the agent-scope publication of the partials costs more
-  // than the split gains at every small workload tried, so one workgroup per
-  // unit is the default.
-  (void)units;
-  (void)waves;
-  return 1;
+int decode_split_auto(int units, int waves, int k, int cus) {
+  // One workgroup per unit, unless the units leave compute units idle and each
+  // share still streams at least kMinRows rows.  Measured on MI355X (32 units,
+  // 8 wavefronts per workgroup): 8 shares of 512 or 1024 rows ran 2.7x and 3.4x
+  // faster than one workgroup per unit; shares of 256 rows or fewer lose, the
+  // publication round trips (store acknowledgement, arrival count, reads of the
+  // partials) costing more than the streaming they save.
+  constexpr int kMinRows = 512;
+  if (waves < 8 || units >= cus) return 1;
+  int s = cus / units;
+  if (s > k / kMinRows) s = k / kMinRows;
+  if (s > 64) s = 64;
+  return s < 1 ? 1 : s;
 }
 
 namespace {

@@ -110,7 +110,16 @@ h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** o
   c->scratch = nullptr;
   c->split_mem = nullptr;
   c->split = h2o::SplitScratch{nullptr, nullptr, nullptr, 1};
-  const int splits = cfg->decode_split ? cfg->decode_split : h2o::decode_split_auto((int)units, c->waves);
+  int cus = 256;  // compute units of the current device (MI355X: 256), asked only when
+                  // the automatic choice could split
+  if (!cfg->decode_split && c->waves >= 8 && k >= 1024) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+  }
+  const int splits =
+      cfg->decode_split ? cfg->decode_split : h2o::decode_split_auto((int)units, c->waves, c->k, cus);
   if (cfg->max_prompt > 0) {
     const size_t bytes = (size_t)2 * units * c->stride * sizeof(float);
     const hipError_t e = hipMalloc((void**)&c->scratch, bytes);
@@ -283,6 +292,13 @@ h2o_status h2o_query(const h2o_ctx* ctx, int32_t* next_pos, int32_t* n_live) {
   if (!ctx) return H2O_ERR_INVALID;
   if (next_pos) *next_pos = ctx->t;
   if (n_live) *n_live = ctx->n_live;
+  return H2O_OK;
+}
+
+h2o_status h2o_launch_shape(const h2o_ctx* ctx, int32_t* decode_waves, int32_t* decode_split) {
+  if (!ctx) return H2O_ERR_INVALID;
+  if (decode_waves) *decode_waves = ctx->waves;
+  if (decode_split) *decode_split = ctx->split.splits;
   return H2O_OK;
 }
 

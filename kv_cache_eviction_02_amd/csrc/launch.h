@@ -81,6 +81,6 @@ bool decode_multi_fits(int k, int dtype, int cache, int head_dim, int waves);
 // Automatic wavefronts per unit for the decode kernel.
 int decode_waves_auto(int units);
 // Automatic workgroups per unit (1 = no split).
-int decode_split_auto(int units, int waves);
+int decode_split_auto(int units, int waves, int k, int cus);
 
 }  // namespace h2o

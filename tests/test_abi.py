@@ -39,7 +39,7 @@ def test_library_exports_every_header_function():
     names = header_functions()
     assert names == sorted(["h2o_create", "h2o_prefill", "h2o_prefill_with_output",
                             "h2o_decode_step", "h2o_decode_steps",
-                            "h2o_query", "h2o_destroy", "h2o_status_string"])
+                            "h2o_query", "h2o_launch_shape", "h2o_destroy", "h2o_status_string"])
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -152,6 +152,7 @@ def test_call_order_and_argument_checks_without_device_work():
         assert k2.h2o_destroy(ctx) == B.H2O_OK
     assert k2.h2o_destroy(None) == B.H2O_OK
     assert B.load_library().h2o_query(None, None, None) == B.H2O_ERR_INVALID
+    assert B.load_library().h2o_launch_shape(None, None, None) == B.H2O_ERR_INVALID
 
 
 def test_adopted_state_counters():
@@ -222,3 +223,17 @@ def test_lds_budget_of_large_e4m3_budget():
     st, ctx = k2.h2o_create(cfg(decode_waves=4, **base), state(ks=FAKE, vs=FAKE))
     assert st == B.H2O_OK and ctx
     assert k2.h2o_destroy(ctx) == B.H2O_OK
+
+
+def test_launch_shape_reports_the_automatic_choices():
+    # small budgets never split (each share would keep fewer than 512 rows) and
+    # the automatic wave count fills about four wavefronts per SIMD
+    for kw, want in [(dict(), (8, 1)), (dict(decode_waves=2), (2, 1)),
+                     (dict(batch=64, heads=56), (1, 1)),
+                     (dict(recent=1024, heavy=1024, decode_waves=4), (4, 1))]:
+        st, ctx = k2.h2o_create(cfg(**kw), state())
+        assert st == B.H2O_OK, kw
+        try:
+            assert k2.h2o_launch_shape(ctx) == (B.H2O_OK, *want), kw
+        finally:
+            assert k2.h2o_destroy(ctx) == B.H2O_OK
