@@ -152,13 +152,47 @@ struct Stash {
   float ring_scale[2];     // E4M3 row scales of the ring row
 };
 
+// Row batches base = lo, lo + NG, ... below hi, with the loads of DEPTH - 1
+// batches in flight while one is consumed.  Loads are issued unconditionally,
+// also for up to DEPTH - 1 batches past hi (the callers' fetch re-reads a valid
+// row there), so every index into the register ring is a compile-time
+// constant; consumption stops at the first batch past hi (a wave-uniform exit).
+template <int DEPTH, int NG, typename Buf, typename F, typename C>
+__device__ __forceinline__ void row_pipeline(int lo, int hi, F&& fetch, C&& consume) {
+  Buf b[DEPTH];
+#pragma unroll
+  for (int i = 0; i + 1 < DEPTH; ++i) fetch(lo + i * NG, b[i]);
+  for (int base = lo; base < hi; base += DEPTH * NG) {
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) {
+      if (base + i * NG >= hi) break;
+      fetch(base + (i + DEPTH - 1) * NG, b[(i + DEPTH - 1) % DEPTH]);
+      consume(base + i * NG, b[i]);
+    }
+  }
+}
+
+struct RowBuf {
+  uint4 k, v;
+};
+struct QuantRowBuf {
+  uint4 k, v;
+  float ks, vs;
+};
+
+// Row batches in flight per wavefront.  With 8 wavefronts per workgroup the
+// launch has few wavefronts per SIMD (few units, or a split over few units),
+// so each keeps three batches of loads in flight; otherwise one.
+template <typename GG>
+constexpr int stream_depth() { return GG::NT / 64 >= 8 ? 4 : 2; }
+
 // Streams logical rows [lo, hi): logit of each row into s_logit[j] (log2
 // domain), per-row-group online softmax into (m, lsum, o).  The rows the
 // admission writes are copied into the LDS stash when they fall in the range.
 // Loads are unconditional (rows outside the range and idle lanes re-read a
 // valid row and are masked out) so the compiler tracks outstanding loads
 // exactly; the next row batch is in flight while the current one is consumed.
-template <typename GG>
+template <typename GG, int DEPTH = stream_depth<GG>()>
 __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG>& u, int lo, int hi,
                                             const float* qf, float scale_log2, float* s_logit,
                                             Stash<GG>* st, float& m, float& lsum, float* o) {
@@ -171,7 +205,7 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
   const int chunk = act ? gl : 0;
 
   if constexpr (!GG::kQuant) {
-    auto fetch = [&](int base, uint4& kr, uint4& vr) {
+    auto fetch = [&](int base, RowBuf& b) {
       const int j = base + grp;
       const char* kp = u.kn;
       const char* vp = u.vn;
@@ -180,10 +214,12 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
         kp = u.K + off;
         vp = u.V + off;
       }
-      kr = load16_stream(kp + chunk * 16);
-      vr = load16_stream(vp + chunk * 16);
+      b.k = load16_stream(kp + chunk * 16);
+      b.v = load16_stream(vp + chunk * 16);
     };
-    auto consume = [&](int base, const uint4& kr, const uint4& vr) {
+    auto consume = [&](int base, const RowBuf& b) {
+      const uint4& kr = b.k;
+      const uint4& vr = b.v;
       float kf[EPL];
       EC::unpack(kr, kf);
       float d = 0.f;
@@ -221,14 +257,7 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
         for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vf[e], o[e]);
       }
     };
-    uint4 ka, va, kb, vb;
-    fetch(lo, ka, va);
-    for (int base = lo; base < hi; base += 2 * NG) {
-      fetch(base + NG, kb, vb);
-      consume(base, ka, va);
-      fetch(base + 2 * NG, ka, va);
-      consume(base + NG, kb, vb);
-    }
+    row_pipeline<DEPTH, NG, RowBuf>(lo, hi, fetch, consume);
   } else {
     // The decoded token (exact bf16 row) seeds row group 0 when it is in range.
     if (v.n_live >= lo && v.n_live < hi) {
@@ -250,16 +279,20 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
       }
     }
     const int end = min(hi, v.n_live);  // cached rows only
-    auto fetch = [&](int base, uint4& kr, uint4& vr, float& ksc, float& vsc) {
+    auto fetch = [&](int base, QuantRowBuf& b) {
       const int j = base + grp;
       const int s = (j < end) ? v.slot_of(j) : 0;  // slot 0 stands in past the end
       const size_t off = (size_t)s * GG::ROWB;
-      kr = load16_stream(u.K + off + chunk * 16);
-      vr = load16_stream(u.V + off + chunk * 16);
-      ksc = u.ks[s];
-      vsc = u.vs[s];
+      b.k = load16_stream(u.K + off + chunk * 16);
+      b.v = load16_stream(u.V + off + chunk * 16);
+      b.ks = u.ks[s];
+      b.vs = u.vs[s];
     };
-    auto consume = [&](int base, const uint4& kr, const uint4& vr, float ksc, float vsc) {
+    auto consume = [&](int base, const QuantRowBuf& b) {
+      const uint4& kr = b.k;
+      const uint4& vr = b.v;
+      const float ksc = b.ks;
+      const float vsc = b.vs;
       float kf[EPL];
       EC::unpack(kr, kf);
       float d = 0.f;
@@ -299,15 +332,7 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
         for (int e = 0; e < EPL; ++e) o[e] = fmaf(pv, vf[e], o[e]);
       }
     };
-    uint4 ka, va, kb, vb;
-    float ska, sva, skb, svb;
-    fetch(lo, ka, va, ska, sva);
-    for (int base = lo; base < end; base += 2 * NG) {
-      fetch(base + NG, kb, vb, skb, svb);
-      consume(base, ka, va, ska, sva);
-      fetch(base + 2 * NG, ka, va, ska, sva);
-      consume(base + NG, kb, vb, skb, svb);
-    }
+    row_pipeline<DEPTH, NG, QuantRowBuf>(lo, end, fetch, consume);
   }
 }
 
