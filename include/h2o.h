@@ -42,6 +42,9 @@
  *   - A ctx is not thread-safe; calls on one ctx must be serialised by the
  *     caller, and consecutive calls must go to the same stream (or be ordered
  *     by the caller) because each step reads what the previous one wrote.
+ *   - A ctx belongs to the device that is current at h2o_create (its scratch
+ *     lives there): later calls must run with that device current, and their
+ *     buffers and stream must be on it.
  *   - Device faults are reported by the caller's next synchronisation.
  */
 #ifndef H2O_H
