@@ -30,12 +30,13 @@
 //   may move to the victim's slot and the new token's row are kept in LDS from
 //   the streaming pass, so admission writes at most two rows.
 //
-// decode_split_kernel: for batches with few units, S workgroups share a unit,
-//   each streaming a contiguous range of its rows.  Every workgroup writes its
-//   partial (max, sum, output) and its logits to scratch and increments the
-//   unit's arrival counter; the last to arrive combines the partials, runs the
-//   score update and eviction, and resets the counter.  No workgroup waits for
-//   another.
+// decode_split_kernel: for batches with few units and long contexts, S
+//   workgroups share a unit, each streaming a contiguous range of its rows.
+//   Every workgroup writes its partial (max, sum, output) and its logits to
+//   scratch with device-scope stores and increments the unit's arrival counter;
+//   the last to arrive reads them back with device-scope loads, combines the
+//   partials, runs the score update and eviction, and resets the counter.  No
+//   workgroup waits for another and no cache is written back.
 //
 // decode_multi_kernel: n steps over tokens known in advance in one launch; each
 //   workgroup carries its unit from step to step with the scores and positions
