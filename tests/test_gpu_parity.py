@@ -530,3 +530,37 @@ def test_random_configurations(wl, cache, policy, split, waves, output):
     stats = run_workload(wl, wl.units, wl.steps, kv_every=1, decode_split=split, decode_waves=waves,
                          cache=cache, prompt_output=output, policy=policy)
     assert stats.steps == wl.steps
+
+
+def _random_medium_cases(n=16, seed=77):
+    """Larger random configurations: prompts of several prefill blocks with a
+    ragged tail, budgets of hundreds of slots (several row batches per
+    wavefront, a ring that wraps many times), automatic launch shapes."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 96, 128]))
+        kv = "f32" if rng.random() < 0.25 else "bf16"
+        cache = "e4m3" if kv == "bf16" and rng.random() < 0.35 else "input"
+        recent = int(rng.integers(0, 400))
+        heavy = int(rng.integers(0, 800))
+        if recent + heavy == 0:
+            heavy = 64
+        prompt = int(rng.integers(100, 1500))
+        steps = int(rng.integers(40, 160))
+        skew = str(rng.choice(["fraction", "zipf", "bursts"]))
+        wl = Workload(400 + i, f"rand_medium{i:02d}", int(rng.integers(1, 3)), int(rng.integers(1, 4)), d,
+                      prompt, steps, recent, heavy, kv, skew, skew_frac=0.05, zipf_alpha=1.1)
+        policy = str(rng.choice(["h2o", "h2o", "static", "naive"]))
+        split = int(rng.choice([0, 0, 1, 3]))
+        output = bool(rng.random() < 0.25)
+        cases.append((wl, cache, policy, split, output))
+    return cases
+
+
+@pytest.mark.parametrize("wl,cache,policy,split,output", _random_medium_cases(),
+                         ids=lambda v: v.name if isinstance(v, Workload) else None)
+def test_random_medium_configurations(wl, cache, policy, split, output):
+    stats = run_workload(wl, wl.units, wl.steps, kv_every=16, decode_split=split, cache=cache,
+                         prompt_output=output, policy=policy)
+    assert stats.steps == wl.steps
