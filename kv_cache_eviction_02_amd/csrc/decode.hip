@@ -69,6 +69,31 @@ __device__ inline unsigned long long shfl_xor_u64(unsigned long long x, int mask
   return ((unsigned long long)hi << 32) | lo;
 }
 
+template <int CTRL>
+__device__ inline unsigned long long dpp_u64(unsigned long long x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, false);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Minimum over the 64 lanes, in every lane: DPP within each row of 16 lanes
+// (quad swaps, then the half-row and row mirrors), then two cross-row shuffles.
+__device__ inline unsigned long long wave_min_u64(unsigned long long w) {
+  unsigned long long o;
+  o = dpp_u64<kDppQuadXor1>(w);
+  w = o < w ? o : w;
+  o = dpp_u64<kDppQuadXor2>(w);
+  w = o < w ? o : w;
+  o = dpp_u64<kDppHalfMirror>(w);
+  w = o < w ? o : w;
+  o = dpp_u64<kDppRowMirror>(w);
+  w = o < w ? o : w;
+  o = shfl_xor_u64(w, 16);
+  w = o < w ? o : w;
+  o = shfl_xor_u64(w, 32);
+  return o < w ? o : w;
+}
+
 // T: input element type (q, k_new, v_new); C: cache element type.
 template <typename T, typename C, int D, int NW>
 struct Geo {
@@ -421,9 +446,9 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
     best = ((unsigned long long)__float_as_uint(p_self) << 32) | (uint32_t)v.t;
     best_slot = kSelfVictim;
   }
-  auto update = [&](int j, float old, int ps) {
+  auto update = [&](int j, float lg, float old, int ps) {
     const int s = v.slot_of(j);
-    const float ns = (naive ? 0.f : old) + fast_exp2(s_logit[j] - M) * invL;
+    const float ns = (naive ? 0.f : old) + fast_exp2(lg - M) * invL;
     s_logit[j] = ns;
     if (v.is_cand(s)) {
       const unsigned long long key = ((unsigned long long)__float_as_uint(ns) << 32) | (uint32_t)ps;
@@ -432,27 +457,32 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
         best_slot = s;
       }
     }
+    return ns;
   };
+  // The prefetched slots: all logits are read before any new score is written
+  // back, so the LDS reads are in flight together; the new scores stay in
+  // registers for the stores below.
+  float ns_pf[PF];
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
     const int j = tid + i * NT;
-    if (j < v.n_live) update(j, sc_pf[i], ps_pf[i]);
+    ns_pf[i] = j < v.n_live ? s_logit[j] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int j = tid + i * NT;
+    if (j < v.n_live) ns_pf[i] = update(j, ns_pf[i], sc_pf[i], ps_pf[i]);
   }
   for (int j = tid + PF * NT; j < v.n_live; j += NT) {
     const int s = v.slot_of(j);
-    update(j, u.score[s], v.is_cand(s) ? u.pos[s] : 0);
+    update(j, s_logit[j], u.score[s], v.is_cand(s) ? u.pos[s] : 0);
   }
 
   unsigned long long vkey = ~0ull;
   if (v.full && !argmin) {
     vkey = (uint32_t)v.fixed_victim_pos();  // s_victim keeps its initial fixed_victim()
   } else if (v.full) {
-    unsigned long long w = best;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const unsigned long long other = shfl_xor_u64(w, off);
-      w = other < w ? other : w;
-    }
+    const unsigned long long w = wave_min_u64(best);
     if (lane == 0) s_key[wave] = w;
     __syncthreads();
 #pragma unroll
@@ -477,16 +507,16 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
     adm = v.full ? (*s_victim == kSelfVictim ? -1 : *s_victim) : v.n_live;
   }
 
-  auto write_score = [&](int j) {
+  auto write_score = [&](int j, float ns) {
     const int s = v.slot_of(j);
-    if (s != adm && s != dst) u.score[s] = s_logit[j];
+    if (s != adm && s != dst) u.score[s] = ns;
   };
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
     const int j = tid + i * NT;
-    if (j < v.n_live) write_score(j);
+    if (j < v.n_live) write_score(j, ns_pf[i]);
   }
-  for (int j = tid + PF * NT; j < v.n_live; j += NT) write_score(j);
+  for (int j = tid + PF * NT; j < v.n_live; j += NT) write_score(j, s_logit[j]);
 
   if (tid == 0) {
     if (dst >= 0) {
