@@ -223,7 +223,8 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
                       wl.scale, device=dev, decode_waves=waves, decode_split=split, cache=cache_kind,
                       policy=policy, steps_mode="persistent")
         pc.prefill(*prompt_keep)
-        pc.steps(dq[:warmup], dk[:warmup], dv[:warmup])
+        if warmup:
+            pc.steps(dq[:warmup], dk[:warmup], dv[:warmup])
         torch.cuda.synchronize()
         r0.record(stream)
         pc.steps(dq[warmup:warmup + steps], dk[warmup:warmup + steps], dv[warmup:warmup + steps],
@@ -314,9 +315,10 @@ def main():
     if args.heavy_only:
         wl = dataclasses.replace(wl, recent=0, heavy=wl.k)
     modified = bool(args.prompt or args.budget or args.heavy_only)
-    steps = args.steps
-    warmup = args.warmup
+    steps = max(1, args.steps)
+    warmup = max(0, args.warmup)
     if warmup + steps > wl.steps:
+        warmup = min(warmup, wl.steps - 1)
         steps = max(1, wl.steps - warmup)
         print(f"[bench] {wl.name} has {wl.steps} decode positions: timing {steps} steps",
               file=sys.stderr, flush=True)
