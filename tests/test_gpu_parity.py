@@ -128,8 +128,24 @@ def test_neox20b_full_batch_sampled_units():
     run_workload(WORKLOADS["neox20b"], 6, 48, kv_every=16)
 
 
-def test_llama7b_long_stream():
-    run_workload(WORKLOADS["llama7b_stream"], 4, 20_000, check_every=50, kv_every=2500)
+# ---- the full decode lengths of the three large workloads and the long stream ------
+# Every step of the workload runs on the GPU in the per-step launch shape the
+# benchmark times; the oracle checks a sample of units at a sample of steps.
+
+def test_opt30b_full_length():
+    wl = WORKLOADS["opt30b"]
+    run_workload(wl, 8, wl.steps, check_every=16, kv_every=256)
+
+
+def test_neox20b_full_length():
+    wl = WORKLOADS["neox20b"]
+    run_workload(wl, 4, wl.steps, check_every=32, kv_every=512)
+
+
+def test_llama7b_stream_full_length():
+    wl = WORKLOADS["llama7b_stream"]
+    assert wl.steps == 200_000
+    run_workload(wl, 4, wl.steps, check_every=250, kv_every=25_000)
 
 
 # ---- launch shapes ------------------------------------------------------------------
