@@ -151,6 +151,32 @@ def cpu_baseline(wl, units_per_worker, steps, policy="h2o"):
 
 # ---- GPU -----------------------------------------------------------------------
 
+def time_torch_flash_attention(prompt, scale, stream, reps=5):
+    """Mean time (ms) of torch's flash-attention forward, causal, over the same prompt
+    q, k, v ([B, H, P, d] bf16): a measured reference for the prompt-output prefill.
+    Only the flash backend is allowed, so nothing falls back to batched products;
+    None when that backend is not available."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    q, k, v = prompt
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            o = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                o = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        del o
+        return e0.elapsed_time(e1) / reps
+    except RuntimeError as ex:
+        print(f"[bench] torch flash attention unavailable: {ex}", file=sys.stderr, flush=True)
+        return None
+
+
 def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, cache="input",
             policy="h2o", streaming=True):
     import torch
@@ -193,8 +219,13 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     p1.record(stream)
     torch.cuda.synchronize()
     prefill_out_ms = p0.elapsed_time(p1)
+    del prompt_out
+    # torch's own causal flash attention over the same prompt, for context (not in
+    # counter runs, whose only copies calibrate the byte counters)
+    sdpa_ms = time_torch_flash_attention(prompt, wl.scale, stream) \
+        if wl.kv_dtype == "bf16" and not copy_mib else None
     prompt_keep = prompt if streaming and not single_calls else None
-    del prompt, prompt_out
+    del prompt
 
     for s in range(warmup):
         cache.step(dq[s], dk[s], dv[s])
@@ -269,7 +300,7 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     if clock:
         device["clock_mhz"] = clock / 1000
     return dict(region_ms=region_ms, stream_ms=stream_ms, prefill_ms=prefill_ms, prefill_out_ms=prefill_out_ms,
-                waves=waves_used, split=split_used, device=device, copy_gbs=copy_gbs)
+                sdpa_ms=sdpa_ms, waves=waves_used, split=split_used, device=device, copy_gbs=copy_gbs)
 
 
 def main():
@@ -387,6 +418,13 @@ def main():
                 # causal QK^T and PV: each P(P+1)/2 dot products of length d per unit
                 "tflops": 2 * prefill_flops(wl) / (g["prefill_out_ms"] * 1e-3) / 1e12,
                 "out_bytes": wl.units * wl.prompt * wl.head_dim * 4,
+                # the same causal QK^T and PV by torch (no column sums, no selection,
+                # bf16 output): a measured reference, not part of the path
+                "torch_flash_attention": None if g["sdpa_ms"] is None else {
+                    "kind": "torch.nn.functional.scaled_dot_product_attention, flash backend, causal",
+                    "ms": g["sdpa_ms"],
+                    "tflops": 2 * prefill_flops(wl) / (g["sdpa_ms"] * 1e-3) / 1e12,
+                },
             },
         },
         "streaming": None if g["stream_ms"] is None else {
