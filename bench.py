@@ -151,6 +151,46 @@ def cpu_baseline(wl, units_per_worker, steps, policy="h2o"):
 
 # ---- GPU -----------------------------------------------------------------------
 
+def read_ceiling(stream, gib=4, reps=3):
+    """Best HBM read rate (GB/s) of the streaming-read probe (libh2o_probe.so,
+    16-byte non-temporal loads, grid-stride) over `gib` GiB, and the workgroup
+    count that reached it; None when the probe library is not built."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "kv_cache_eviction_02_amd", "libh2o_probe.so")
+    if not os.path.exists(path):
+        print(f"[bench] {path} missing: no read ceiling", file=sys.stderr, flush=True)
+        return None
+    lib = ctypes.CDLL(path)
+    lib.h2o_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.h2o_probe_read.restype = ctypes.c_int
+    nbytes = gib << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    assert src.data_ptr() % 16 == 0 and nbytes % 16 == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = (0.0, 0)
+    # up to one 16-byte load per thread (2^20 workgroups over 4 GiB), the best shape measured
+    for blocks in (4096, 16384, 65536, 262144, 1 << 20):
+        def run():
+            st = lib.h2o_probe_read(src.data_ptr(), nbytes, sink.data_ptr(), blocks, stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"h2o_probe_read returned {st}")
+        run()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbs = reps * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        best = max(best, (gbs, blocks))
+    del src, sink
+    return best
+
+
 def time_torch_flash_attention(prompt, scale, stream, reps=5):
     """Mean time (ms) of torch's flash-attention forward, causal, over the same prompt
     q, k, v ([B, H, P, d] bf16): a measured reference for the prompt-output prefill.
@@ -281,6 +321,9 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
         torch.cuda.synchronize()
         copy_gbs = 5 * 2 * xc.numel() * 2 / (r0.elapsed_time(r1) * 1e-3) / 1e9
         del xc, yc
+        read_best = read_ceiling(stream)
+    else:
+        read_best = None
     if copy_mib:
         # plain device copy of known size, for scaling the HBM byte counters
         x = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -300,7 +343,7 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     if clock:
         device["clock_mhz"] = clock / 1000
     return dict(region_ms=region_ms, stream_ms=stream_ms, prefill_ms=prefill_ms, prefill_out_ms=prefill_out_ms,
-                sdpa_ms=sdpa_ms, waves=waves_used, split=split_used, device=device, copy_gbs=copy_gbs)
+                sdpa_ms=sdpa_ms, read_best=read_best, waves=waves_used, split=split_used, device=device, copy_gbs=copy_gbs)
 
 
 def main():
@@ -440,6 +483,12 @@ def main():
         "copy_ceiling": None if g["copy_gbs"] is None else {
             "kind": "device-to-device copy, 2 GiB read + 2 GiB written (torch)",
             "GBps": g["copy_gbs"], "frac": g["copy_gbs"] / PEAK_HBM_GBS},
+        "read_ceiling": None if g["read_best"] is None else {
+            "kind": "hand-written streaming read, 16-byte non-temporal loads, grid-stride, 4 GiB, "
+                    "best of 2^12-2^20 workgroups of 256 threads (libh2o_probe.so)",
+            "GBps": g["read_best"][0], "frac": g["read_best"][0] / PEAK_HBM_GBS,
+            "workgroups": g["read_best"][1],
+            "decode_frac_of_ceiling": achieved / g["read_best"][0]},
         "cpu_baseline": cpu,
         "device": g["device"],
     }

@@ -1,5 +1,6 @@
 """Build step of the H2O library: compiles the HIP kernels and the C ABI into
-kv_cache_eviction_02_amd/libh2o.so for gfx950 with hipcc.
+kv_cache_eviction_02_amd/libh2o.so for gfx950 with hipcc, and the benchmark's
+streaming-read probe (not part of the H2O path) into libh2o_probe.so.
 
     python -m kv_cache_eviction_02_amd.build
 """
@@ -13,6 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libh2o.so")
 SOURCES = ["h2o_api.cpp", "decode.hip", "prefill.hip"]
+PROBE_LIB = os.path.join(PKG, "libh2o_probe.so")
+PROBE_SOURCES = ["read_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -23,14 +26,14 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose=False) -> str:
-    tmp = LIB + ".tmp"
+def _compile(sources, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-function",
            # keep the compiler from forming packed fp32 instructions
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,7 +42,14 @@ def build(verbose=False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
     if verbose and errs:
         print("\n".join(errs), file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose=False) -> str:
+    """Compile libh2o.so and the benchmark's probe library; returns libh2o.so's path."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
     return LIB
 
 

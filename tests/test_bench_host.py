@@ -61,3 +61,20 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "only --gpus 1" in r.stderr
+
+
+def test_read_probe_library_exports_and_rejects_bad_arguments():
+    """The benchmark's streaming-read probe is built beside libh2o and refuses
+    invalid arguments before any HIP call."""
+    import ctypes
+    path = os.path.join(ROOT, "kv_cache_eviction_02_amd", "libh2o_probe.so")
+    assert os.path.exists(path), "build the libraries first (python -m kv_cache_eviction_02_amd.build)"
+    lib = ctypes.CDLL(path)
+    f = lib.h2o_probe_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(None, 1024, 16, 1024, None) == 1          # no source
+    assert f(16, 1024, None, 1024, None) == 1          # no sink
+    assert f(16, 1000, 16, 1024, None) == 1            # not whole 16-byte chunks
+    assert f(24, 1024, 16, 1024, None) == 1            # misaligned source
+    assert f(16, 1024, 16, 0, None) == 1               # no workgroups
