@@ -637,12 +637,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 // do the outputs.  Rows admitted at one step are read at the next by other
 // threads of the same workgroup: the workgroup barrier between steps orders
 // them.
-// With one or two wavefronts per unit (large batches), four waves per SIMD:
-// a unit whose workgroup is not resident would wait for whole launches of the
-// others (3584 single-wave units need 3.5 per SIMD).  Small batches use more
-// wavefronts per unit and are not bounded by residency.
+// With up to four wavefronts per unit (more than 512 units), four waves per
+// SIMD: a unit whose workgroup is not resident would wait for whole launches
+// of the others (3584 single-wave units need 3.5 per SIMD, 1024 four-wave
+// units 4).  Eight-wavefront units (small batches) are not bounded.
 template <typename T, typename C, int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 2 ? 4 : 1))) void decode_multi_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 4 ? 4 : 1))) void decode_multi_kernel(
     DecodeArgs a, int n_steps, int live0) {
   using GG = Geo<T, C, D, NW>;
   __shared__ StepShared<GG, D> sh;
