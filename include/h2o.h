@@ -102,11 +102,13 @@ typedef enum { H2O_POLICY_H2O = 0, H2O_POLICY_STATIC = 1, H2O_POLICY_NAIVE = 2 }
  * launch carries every (batch, head) unit through all n steps, keeping its
  * scores and positions in LDS between steps; it pays off when a step moves
  * little data (launch and tail latency dominate) and loses to per-step
- * launches on large batches.  H2O_STEPS_PER_STEP: one launch per step.
- * H2O_STEPS_AUTO: persistent when the cached K/V rows of one step total at
- * most 64 MiB, else per step.  Persistent launches also need decode_split = 1
- * and the unit's 3k + 1 words of LDS; otherwise one launch per step is used.
- * Results are bit-identical in every mode. */
+ * launches with single-wavefront units on large batches.  H2O_STEPS_PER_STEP:
+ * one launch per step.  H2O_STEPS_AUTO: persistent when every unit's workgroup
+ * fits on the device at once (the runtime's occupancy for the kernel) and
+ * either the decode runs several wavefronts per unit or the cached K/V rows
+ * of one step total at most 64 MiB; else per step.  Persistent launches also
+ * need decode_split = 1 and the unit's 3k + 1 words of LDS; otherwise one
+ * launch per step is used.  Results are bit-identical in every mode. */
 typedef enum { H2O_STEPS_AUTO = 0, H2O_STEPS_PER_STEP = 1, H2O_STEPS_PERSISTENT = 2 } h2o_steps_mode;
 
 /* Longest prompt a ctx can be created for (max_prompt). */

@@ -817,6 +817,37 @@ hipError_t launch_multi_nw(const DecodeArgs& a, int n_steps, int live0, hipStrea
   return hipGetLastError();
 }
 
+template <typename T, typename C, int D, int NW>
+int multi_per_cu_nw(int k) {
+  int n = 0;
+  const size_t lds = (size_t)(3 * k + 1) * sizeof(float);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_multi_kernel<T, C, D, NW>, NW * 64, lds) !=
+      hipSuccess)
+    return 0;
+  return n;
+}
+
+template <typename T, typename C, int D>
+int multi_per_cu_d(int k, int waves) {
+  switch (waves) {
+    case 1: return multi_per_cu_nw<T, C, D, 1>(k);
+    case 2: return multi_per_cu_nw<T, C, D, 2>(k);
+    case 4: return multi_per_cu_nw<T, C, D, 4>(k);
+    case 8: return multi_per_cu_nw<T, C, D, 8>(k);
+    default: return 0;
+  }
+}
+
+template <typename T, typename C>
+int multi_per_cu_t(int k, int head_dim, int waves) {
+  switch (head_dim) {
+    case 64: return multi_per_cu_d<T, C, 64>(k, waves);
+    case 96: return multi_per_cu_d<T, C, 96>(k, waves);
+    case 128: return multi_per_cu_d<T, C, 128>(k, waves);
+    default: return 0;
+  }
+}
+
 template <typename T, typename C, int D>
 hipError_t launch_multi_d(const DecodeArgs& a, int waves, int n_steps, int live0, hipStream_t s) {
   switch (waves) {
@@ -924,6 +955,14 @@ size_t decode_static_lds(int dtype, int cache, int head_dim, int waves) {
 bool decode_multi_fits(int k, int dtype, int cache, int head_dim, int waves) {
   // logits, scores and positions of the unit in LDS: 3k + 1 words
   return decode_static_lds(dtype, cache, head_dim, waves) + (size_t)(3 * k + 1) * 4 <= kMaxLds;
+}
+
+int decode_multi_per_cu(int k, int dtype, int cache, int head_dim, int waves) {
+  if (!decode_multi_fits(k, dtype, cache, head_dim, waves)) return 0;
+  if (cache == 1) return dtype == 1 ? multi_per_cu_t<bf16, e4m3>(k, head_dim, waves) : 0;
+  if (dtype == 0) return multi_per_cu_t<float, float>(k, head_dim, waves);
+  if (dtype == 1) return multi_per_cu_t<bf16, bf16>(k, head_dim, waves);
+  return 0;
 }
 
 hipError_t launch_decode_multi(const DecodeArgs& a, int dtype, int cache, int head_dim, int waves, int n_steps,

@@ -25,6 +25,7 @@ struct h2o_ctx {
   float* scratch;   // 2 * units * stride floats: row log-sum-exp, column sums
   h2o::SplitScratch split;  // split decode scratch (split.splits < 2: unused)
   void* split_mem;
+  int64_t multi_capacity;   // units the multi-step kernel keeps resident at once; -1 = not asked yet
 };
 
 namespace {
@@ -109,6 +110,7 @@ h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** o
   c->stride = (int32_t)(((int64_t)cfg->max_prompt + 15) / 16 * 16);
   c->scratch = nullptr;
   c->split_mem = nullptr;
+  c->multi_capacity = -1;
   c->split = h2o::SplitScratch{nullptr, nullptr, nullptr, 1};
   int cus = 256;  // compute units of the current device (MI355X: 256), asked only when
                   // the automatic choice could split
@@ -262,8 +264,28 @@ h2o_status h2o_decode_steps(h2o_ctx* ctx, int32_t n_steps, const void* q, const 
   const size_t row_bytes = (size_t)ctx->cfg.head_dim *
                            (ctx->cfg.cache_dtype == H2O_CACHE_E4M3 ? 1 : ctx->cfg.kv_dtype == H2O_BF16 ? 2 : 4);
   const size_t step_bytes = (size_t)ctx->cfg.batch * ctx->cfg.heads * ctx->k * 2 * row_bytes;
-  const bool persistent = ctx->cfg.steps_mode == H2O_STEPS_PERSISTENT ||
-                          (ctx->cfg.steps_mode == H2O_STEPS_AUTO && step_bytes <= ((size_t)64 << 20));
+  const size_t n_units = (size_t)ctx->cfg.batch * ctx->cfg.heads;
+  bool persistent = ctx->cfg.steps_mode == H2O_STEPS_PERSISTENT;
+  if (ctx->cfg.steps_mode == H2O_STEPS_AUTO && n_steps > 1 && ctx->split.splits < 2 &&
+      (ctx->waves > 1 || step_bytes <= ((size_t)64 << 20))) {
+    // Automatic: one launch when every unit's workgroup is resident at once
+    // (else a unit waits for whole launches of the others), and either the
+    // decode has several wavefronts per unit or a step moves little data.
+    // Measured on MI355X: ahead of per-step launches at 2, 4 and 8 wavefronts
+    // per unit on every workload tried, behind with single-wave units of a
+    // bf16 cache (3584 units, k = 410: 127 against 117 us per step).
+    if (ctx->multi_capacity < 0) {
+      const int per_cu = h2o::decode_multi_per_cu(ctx->k, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype,
+                                                  ctx->cfg.head_dim, ctx->waves);
+      int dev = 0, cus = 0;
+      ctx->multi_capacity =
+          per_cu > 0 && hipGetDevice(&dev) == hipSuccess &&
+                  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0
+              ? (int64_t)per_cu * cus
+              : 0;
+    }
+    persistent = (int64_t)n_units <= ctx->multi_capacity;
+  }
   if (n_steps > 1 && persistent && ctx->split.splits < 2 &&
       h2o::decode_multi_fits(ctx->k, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype, ctx->cfg.head_dim, ctx->waves)) {
     // one launch carries every unit through all n_steps
@@ -275,14 +297,13 @@ h2o_status h2o_decode_steps(h2o_ctx* ctx, int32_t n_steps, const void* q, const 
     ctx->n_live = (int64_t)ctx->n_live + n_steps < ctx->k ? ctx->n_live + n_steps : ctx->k;
     return H2O_OK;
   }
-  const size_t units = (size_t)ctx->cfg.batch * ctx->cfg.heads;
-  const size_t in_step = units * ctx->cfg.head_dim * (ctx->cfg.kv_dtype == H2O_BF16 ? 2 : 4);
-  const size_t out_step = units * ctx->cfg.head_dim;
+  const size_t in_step = n_units * ctx->cfg.head_dim * (ctx->cfg.kv_dtype == H2O_BF16 ? 2 : 4);
+  const size_t out_step = n_units * ctx->cfg.head_dim;
   for (int32_t s = 0; s < n_steps; ++s) {
     const h2o_status st = enqueue_step(
         ctx, (const char*)q + s * in_step, (const char*)k_new + s * in_step,
         (const char*)v_new + s * in_step, out + s * out_step,
-        evicted_pos ? evicted_pos + s * units : nullptr, (hipStream_t)stream);
+        evicted_pos ? evicted_pos + s * n_units : nullptr, (hipStream_t)stream);
     if (st != H2O_OK) return st;
   }
   return H2O_OK;

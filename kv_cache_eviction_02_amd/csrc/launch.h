@@ -77,6 +77,9 @@ constexpr size_t kMaxLds = 64 * 1024;
 // kernels add (live slots + 1) * 4 bytes, the multi-step kernel (3k + 1) * 4.
 size_t decode_static_lds(int dtype, int cache, int head_dim, int waves);
 bool decode_multi_fits(int k, int dtype, int cache, int head_dim, int waves);
+// Workgroups of the multi-step kernel one compute unit of the current device
+// holds at once (registers, LDS, waves); 0 when it does not fit or the query fails.
+int decode_multi_per_cu(int k, int dtype, int cache, int head_dim, int waves);
 
 // Automatic wavefronts per unit for the decode kernel.
 int decode_waves_auto(int units);

@@ -331,7 +331,8 @@ def test_run_twice_bitwise_identical():
                            b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
 
 
-def _steps_vs_single(wl, n, split_at, cache_kind="input", policy="h2o", decode_waves=0, decode_split=1):
+def _steps_vs_single(wl, n, split_at, cache_kind="input", policy="h2o", decode_waves=0, decode_split=1,
+                     steps_mode="persistent"):
     """Run n steps as single h2o_decode_step calls and as h2o_decode_steps calls
     (split at split_at); return both runs' outputs, evictions and final state."""
     from kv_cache_eviction_02_amd import H2OCache
@@ -342,7 +343,7 @@ def _steps_vs_single(wl, n, split_at, cache_kind="input", policy="h2o", decode_w
     for multi in (False, True):
         cache = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy, wl.prompt, dtype, wl.scale,
                          cache=cache_kind, policy=policy, decode_waves=decode_waves, decode_split=decode_split,
-                         steps_mode="persistent" if multi else "per_step")
+                         steps_mode=steps_mode if multi else "per_step")
         cache.prefill(*prompt)
         if multi:
             parts = [(0, split_at), (split_at, n)]
@@ -389,6 +390,18 @@ def test_decode_steps_equals_single_steps(name, n, split_at, cache_kind, policy,
     outputs, evictions and state to the same steps as h2o_decode_step calls."""
     say(f"[parity] decode_steps vs decode_step: {name}, {n} steps, {cache_kind}, {policy}, split {split}")
     a, b = _steps_vs_single(WORKLOADS[name], n, split_at, cache_kind, policy, waves, split)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("cache_kind", ["input", "e4m3"])
+@pytest.mark.parametrize("name", ["neox20b", "opt30b"])
+def test_decode_steps_automatic_mode_equals_single_steps(name, cache_kind):
+    """h2o_decode_steps in the automatic mode at the two large workloads (1024
+    four-wavefront units, where it takes one persistent launch, and 3584
+    single-wavefront units, where it launches per step) is bit-identical to
+    single steps."""
+    a, b = _steps_vs_single(WORKLOADS[name], 12, 5, cache_kind, steps_mode="auto")
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 
