@@ -36,6 +36,7 @@ class Workload:
     period: int = 0
     burst_len: int = 16
     query_amp: float = 1.5
+    softmax_scale: float = 0.0  # 0: the default 1/sqrt(head_dim)
 
     @property
     def k(self) -> int:
@@ -51,7 +52,7 @@ class Workload:
 
     @property
     def scale(self) -> float:
-        return 1.0 / math.sqrt(self.head_dim)
+        return self.softmax_scale if self.softmax_scale > 0 else 1.0 / math.sqrt(self.head_dim)
 
     @property
     def elem_bytes(self) -> int:

@@ -168,6 +168,26 @@ def test_split_decode_tiny_and_opt67b():
     run_workload(WORKLOADS["opt6.7b"], 8, 64, decode_split=3, decode_waves=2, kv_every=8)
 
 
+# ---- softmax scales other than 1/sqrt(d) -----------------------------------------------
+
+@pytest.mark.parametrize("factor", [0.25, 3.0])
+@pytest.mark.parametrize("base", ["ragged_f32_d96", "window1_bf16_d64", "mid_prompt_f32_d128",
+                                  "short_prompt_bf16_d128"])
+def test_softmax_scale_passed_through(base, factor):
+    """The scale given at h2o_create (here a quarter or three times 1/sqrt(d):
+    flatter or sharper attention) reaches every kernel: prefill scores, prompt
+    output, decode output, scores and evictions follow the oracle run with the
+    same scale."""
+    import dataclasses
+    import math
+    wl0 = {w.name: w for w in EDGE}[base]
+    wl = dataclasses.replace(wl0, cid=wl0.cid + (500 if factor < 1 else 600),
+                             name=f"{wl0.name}_scale{factor:g}",
+                             softmax_scale=factor / math.sqrt(wl0.head_dim))
+    for split in (1, 3):
+        run_workload(wl, wl.units, wl.steps, kv_every=4, decode_split=split, prompt_output=split == 1)
+
+
 # ---- edge cases ----------------------------------------------------------------------
 
 EDGE = [
