@@ -166,7 +166,8 @@ h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** o
  * walkthrough", step 1).  q, k, v: [B, H, prompt_len, d] kv_dtype, device,
  * read only.  Overwrites the whole state: scores become the causal-attention
  * column sums of the kept positions, K/V rows are copied into their slots,
- * unused slots get pos = -1 and score = 0.  Afterwards the next decoded
+ * unused slots get pos = -1 and score = 0 (their K/V rows and E4M3 scales are
+ * left as they were and are never read).  Afterwards the next decoded
  * position is prompt_len.  1 <= prompt_len <= max_prompt, else
  * H2O_ERR_INVALID.  Three kernels on `stream`. */
 h2o_status h2o_prefill(h2o_ctx* ctx, const void* q, const void* k, const void* v,

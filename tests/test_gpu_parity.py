@@ -218,6 +218,68 @@ def test_calls_are_ordered_on_the_callers_stream():
         assert torch.equal(a, b)
 
 
+# ---- adopting a state, prefilling a ctx again ----------------------------------------------
+
+@pytest.mark.parametrize("cache_kind", ["input", "e4m3"])
+@pytest.mark.parametrize("name,s1,s2", [("opt6.7b", 37, 20), ("short_prompt_bf16_d128", 3, 20)])
+def test_adopted_state_and_second_prefill(name, s1, s2, cache_kind):
+    """A ctx created on a copy of another ctx's state (start_pos / start_live,
+    also while the cache is still filling) continues bit-identically; a ctx that
+    has decoded and is prefilled again equals a fresh ctx prefilled with the
+    same prompt, and so do their next steps."""
+    from kv_cache_eviction_02_amd import H2OCache
+    wl = {w.name: w for w in EDGE}.get(name) or WORKLOADS[name]
+    n = s1 + s2
+    prompt = stage_prompt(wl, "cuda")
+    dq, dk, dv = stage_decode(wl, 0, n, "cuda")
+
+    def make(**kw):
+        return H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy, wl.prompt, torch.bfloat16,
+                        wl.scale, cache=cache_kind, **kw)
+
+    def state(c):
+        # scores and positions everywhere; rows and row scales of live slots only
+        # (a prefill leaves the rows of unused slots as they were: never read)
+        live = c.pos >= 0
+        st = [c.score, c.pos, c.k_slots.view(torch.uint8)[live], c.v_slots.view(torch.uint8)[live]]
+        if cache_kind == "e4m3":
+            st += [c.k_scale[live], c.v_scale[live]]
+        return [x.clone() for x in st]
+
+    def steps(c, lo, hi):
+        res = []
+        for s in range(lo, hi):
+            o, e = c.step(dq[s], dk[s], dv[s])
+            res += [o.clone(), e.clone()]
+        return res
+
+    a = make()
+    a.prefill(*prompt)
+    steps(a, 0, s1)
+    t, live = a.position()
+    assert t == wl.prompt + s1 and live == min(wl.k, t)
+    copy = [a.k_slots.clone(), a.v_slots.clone(), a.score.clone(), a.pos.clone()]
+    if cache_kind == "e4m3":
+        copy += [a.k_scale.clone(), a.v_scale.clone()]
+    b = make(start_pos=t, start_live=live, state=copy)
+    ra, rb = steps(a, s1, n), steps(b, s1, n)
+    for x, y in zip(ra + state(a), rb + state(b)):
+        assert torch.equal(x, y)
+    b.close()
+
+    fresh = make()
+    fresh.prefill(*prompt)
+    a.prefill(*prompt)
+    assert a.position() == fresh.position() == (wl.prompt, min(wl.k, wl.prompt))
+    for x, y in zip(state(a), state(fresh)):
+        assert torch.equal(x, y)
+    ra, rf = steps(a, 0, s2), steps(fresh, 0, s2)
+    for x, y in zip(ra + state(a), rf + state(fresh)):
+        assert torch.equal(x, y)
+    a.close()
+    fresh.close()
+
+
 # ---- softmax scales other than 1/sqrt(d) -----------------------------------------------
 
 @pytest.mark.parametrize("factor", [0.25, 3.0])
