@@ -218,6 +218,28 @@ def test_calls_are_ordered_on_the_callers_stream():
         assert torch.equal(a, b)
 
 
+# ---- more units than the device holds at once ----------------------------------------------
+
+MANY_UNITS = Workload(111, "many_units_bf16_d64", 128, 64, 64, 40, 10, 8, 8, "bf16", "fraction",
+                      skew_frac=0.1)
+
+
+def test_many_units_parity():
+    """8192 units (B128 x H64, d64): two single-wavefront rounds of workgroups
+    per decode launch; sampled units checked against the oracle at every step."""
+    assert MANY_UNITS.units == 8192
+    run_workload(MANY_UNITS, 8, MANY_UNITS.steps, kv_every=2, prompt_output=True)
+
+
+@pytest.mark.parametrize("cache_kind", ["input", "e4m3"])
+def test_many_units_automatic_steps(cache_kind):
+    """The automatic multi-step mode with more units than stay resident at once
+    (it must launch per step) equals single steps bit for bit."""
+    a, b = _steps_vs_single(MANY_UNITS, 10, 4, cache_kind, steps_mode="auto")
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 # ---- adopting a state, prefilling a ctx again ----------------------------------------------
 
 @pytest.mark.parametrize("cache_kind", ["input", "e4m3"])
