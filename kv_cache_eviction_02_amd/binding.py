@@ -257,7 +257,9 @@ class H2OCache:
         return out
 
     def step(self, q, k_new, v_new, out=None, evicted=None):
-        """One decode step; returns (out [B, H, d] float32, evicted [B, H] int32)."""
+        """One decode step; returns (out [B, H, d] float32, evicted [B, H] int32).
+        Without out / evicted arguments these are the cache's own buffers,
+        overwritten by the next step: clone them to keep a step's results."""
         shape = (self.batch, self.heads, self.head_dim)
         ptrs = [self._input(x, shape, n) for x, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"))]
         out = self.out if out is None else out
