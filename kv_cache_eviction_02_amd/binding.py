@@ -298,6 +298,8 @@ class H2OCache:
 
     def close(self):
         if getattr(self, "ctx", None):
+            # h2o_destroy frees the ctx's scratch: no enqueued call may still use it
+            self.torch.cuda.synchronize(self.device)
             _check(h2o_destroy(self.ctx), "h2o_destroy")
             self.ctx = None
 
