@@ -134,8 +134,9 @@ typedef struct {
   int32_t decode_split;/* decode workgroups per (batch, head) unit: 0 = automatic, 1 = one,
                           2..64 = that many (each streams a share of the rows).  Automatic
                           splits only when the units are fewer than the device's compute
-                          units, the workgroups have 8 wavefronts and every share keeps at
-                          least 512 rows (long contexts at small batch) */
+                          units, the workgroups have 8 wavefronts, k >= 768 and every
+                          share keeps at least 256 rows (long contexts at small
+                          batch) */
   int32_t cache_dtype; /* h2o_cache_dtype */
   int32_t policy;      /* h2o_policy */
   int32_t steps_mode;  /* h2o_steps_mode */

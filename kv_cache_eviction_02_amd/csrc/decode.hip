@@ -701,6 +701,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   __shared__ unsigned long long s_key[NW];
   __shared__ int s_victim;
   __shared__ int s_last;
+  __shared__ float s_pm[64], s_pl[64];  // the partials' maxima and sums (S <= 64)
   extern __shared__ float s_logit[];  // [n_live + 1]
 
   const int S = sp.splits;
@@ -767,42 +768,83 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   __syncthreads();
   if (!s_last) return;
 
-  // Combine the partials.
+  // Combine the partials.  Loads are issued in batches of kBatch before any
+  // of them is used, so the combine costs a few memory round trips instead of
+  // one per partial and per logit; sums keep the order c = 0, 1, ..., S - 1.
+  constexpr int kBatch = 8;
   const float* up = sp.partials + (size_t)unit * S * (D + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < S; ++c) M = fmaxf(M, collect(up + (size_t)c * (D + 2)));
-  float L = 0.f;
-  for (int c = 0; c < S; ++c) {
-    const float* q = up + (size_t)c * (D + 2);
-    L = fmaf(collect(q + 1), fast_exp2(collect(q) - M), L);
-  }
-  const float invL = 1.f / L;
-  for (int d = tid; d < D; d += NT) {
-    float acc = 0.f;
-    for (int c = 0; c < S; ++c) {
-      const float* q = up + (size_t)c * (D + 2);
-      acc = fmaf(collect(q + 2 + d), fast_exp2(collect(q) - M), acc);
-    }
-    a.out[(size_t)unit * D + d] = acc * invL;
-  }
-  // All logits, and the rows the admission writes (still intact: only this
-  // workgroup writes the unit's state).
-  for (int j = tid; j < v.n_att; j += NT) s_logit[j] = collect(lg + j);
+  // The rows the admission writes (still intact: only this workgroup writes
+  // the unit's state) and the partials' maxima and sums go into registers
+  // first, in flight with the logits, and into LDS after them.
+  uint4 row[4] = {};  // K, V of the decoded token (unquantized caches), K, V of the ring row
+  float ring_sc[2] = {0.f, 0.f};
   if (tid < LPR) {
     if constexpr (!GG::kQuant) {
-      st.self[0][tid] = load16(u.kn + tid * 16);
-      st.self[1][tid] = load16(u.vn + tid * 16);
+      row[0] = load16(u.kn + tid * 16);
+      row[1] = load16(u.vn + tid * 16);
     }
     if (v.ring_live) {
-      st.ring[0][tid] = load16(u.K + (size_t)v.ring_slot * ROWB + tid * 16);
-      st.ring[1][tid] = load16(u.V + (size_t)v.ring_slot * ROWB + tid * 16);
+      row[2] = load16(u.K + (size_t)v.ring_slot * ROWB + tid * 16);
+      row[3] = load16(u.V + (size_t)v.ring_slot * ROWB + tid * 16);
     }
   }
   if constexpr (GG::kQuant) {
     if (tid == 0 && v.ring_live) {
-      st.ring_scale[0] = u.ks[v.ring_slot];
-      st.ring_scale[1] = u.vs[v.ring_slot];
+      ring_sc[0] = u.ks[v.ring_slot];
+      ring_sc[1] = u.vs[v.ring_slot];
     }
+  }
+  float pm = 0.f, pl = 0.f;
+  if (tid < S) {
+    pm = collect(up + (size_t)tid * (D + 2));
+    pl = collect(up + (size_t)tid * (D + 2) + 1);
+  }
+  // All logits (indices clamped to the last one; only those below n_att are kept).
+  for (int j0 = tid; j0 < v.n_att; j0 += kBatch * NT) {
+    float lv[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) lv[i] = collect(lg + min(j0 + i * NT, v.n_att - 1));
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (j0 + i * NT < v.n_att) s_logit[j0 + i * NT] = lv[i];
+  }
+  if (tid < S) {
+    s_pm[tid] = pm;
+    s_pl[tid] = pl;
+  }
+  if (tid < LPR) {
+    if constexpr (!GG::kQuant) {
+      st.self[0][tid] = row[0];
+      st.self[1][tid] = row[1];
+    }
+    if (v.ring_live) {
+      st.ring[0][tid] = row[2];
+      st.ring[1][tid] = row[3];
+    }
+  }
+  if constexpr (GG::kQuant) {
+    if (tid == 0 && v.ring_live) {
+      st.ring_scale[0] = ring_sc[0];
+      st.ring_scale[1] = ring_sc[1];
+    }
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int c = 0; c < S; ++c) M = fmaxf(M, s_pm[c]);
+  float L = 0.f;
+  for (int c = 0; c < S; ++c) L = fmaf(s_pl[c], fast_exp2(s_pm[c] - M), L);
+  const float invL = 1.f / L;
+  for (int d = tid; d < D; d += NT) {
+    float acc = 0.f;
+    for (int c0 = 0; c0 < S; c0 += kBatch) {
+      float ov[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) ov[i] = collect(up + (size_t)min(c0 + i, S - 1) * (D + 2) + 2 + d);
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (c0 + i < S) acc = fmaf(ov[i], fast_exp2(s_pm[c0 + i] - M), acc);
+    }
+    a.out[(size_t)unit * D + d] = acc * invL;
   }
   __syncthreads();
   finish_step<GG>(v, u, M, invL, s_logit, sc_pf, ps_pf, &st, s_key, &s_victim, a.evicted, unit);
@@ -914,14 +956,17 @@ int decode_waves_auto(int units) {
 }
 
 int decode_split_auto(int units, int waves, int k, int cus) {
-  // One workgroup per unit, unless the units leave compute units idle and each
-  // share still streams at least kMinRows rows.  Measured on MI355X (32 units,
-  // 8 wavefronts per workgroup): 8 shares of 512 or 1024 rows ran 2.7x and 3.4x
-  // faster than one workgroup per unit; shares of 256 rows or fewer lose, the
-  // publication round trips (store acknowledgement, arrival count, reads of the
-  // partials) costing more than the streaming they save.
-  constexpr int kMinRows = 512;
-  if (waves < 8 || units >= cus) return 1;
+  // One workgroup per unit, unless the units leave compute units idle, the
+  // budget is at least kMinK and each share still streams at least kMinRows
+  // rows.  Measured on MI355X (32 units, 8 wavefronts per workgroup): 8 shares
+  // of 512 or 1024 rows ran 2.6x and 2.8x faster than one workgroup per unit,
+  // 4 shares of 256 rows 1.24x and 3 shares of 256 rows 1.07x; 2 shares of 256
+  // rows (k = 512) and shares of 128 rows lost, the publication round trips
+  // (store acknowledgement, arrival count, reads of the partials) costing more
+  // than the streaming they save.
+  constexpr int kMinRows = 256;
+  constexpr int kMinK = 768;
+  if (waves < 8 || units >= cus || k < kMinK) return 1;
   int s = cus / units;
   if (s > k / kMinRows) s = k / kMinRows;
   if (s > 64) s = 64;

@@ -114,7 +114,7 @@ h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** o
   c->split = h2o::SplitScratch{nullptr, nullptr, nullptr, 1};
   int cus = 256;  // compute units of the current device (MI355X: 256), asked only when
                   // the automatic choice could split
-  if (!cfg->decode_split && c->waves >= 8 && k >= 1024) {
+  if (!cfg->decode_split && c->waves >= 8 && k >= 768) {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)

@@ -226,7 +226,7 @@ def test_lds_budget_of_large_e4m3_budget():
 
 
 def test_launch_shape_reports_the_automatic_choices():
-    # small budgets never split (each share would keep fewer than 512 rows) and
+    # small budgets never split (each share would keep fewer than 256 rows) and
     # the automatic wave count fills about four wavefronts per SIMD
     for kw, want in [(dict(), (8, 1)), (dict(decode_waves=2), (2, 1)),
                      (dict(batch=64, heads=56), (1, 1)),

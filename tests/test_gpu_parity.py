@@ -362,14 +362,14 @@ def test_large_budget(waves, split):
 @pytest.mark.parametrize("cache_kind", ["input", "e4m3"])
 def test_automatic_split_long_context(cache_kind):
     """Few units and a long budget (B1 x H4, k = 2048): the library splits each
-    unit over 4 workgroups of 8 wavefronts by itself (shares of 512 rows),
+    unit over 8 workgroups of 8 wavefronts by itself (shares of 256 rows),
     through the single-step and the multi-step calls."""
     from parity import Harness
     wl = Workload(110, "long_ctx_bf16", 1, 4, 128, 2100, 24, 1024, 1024, "bf16", "zipf", zipf_alpha=1.1)
     say(f"[parity] {wl.name} automatic split, cache={cache_kind}")
     hn = Harness(wl, list(range(wl.units)), wl.steps, cache=cache_kind)
     try:
-        assert hn.cache.launch_shape() == (8, 4)
+        assert hn.cache.launch_shape() == (8, 8)
         hn.prefill()
         stats = hn.run(check_every=1, kv_every=4)
     finally:
