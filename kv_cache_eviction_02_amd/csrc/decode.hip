@@ -701,7 +701,6 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   __shared__ unsigned long long s_key[NW];
   __shared__ int s_victim;
   __shared__ int s_last;
-  __shared__ float s_pm[64], s_pl[64];  // the partials' maxima and sums (S <= 64)
   extern __shared__ float s_logit[];  // [n_live + 1]
 
   const int S = sp.splits;
@@ -771,6 +770,12 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   // Combine the partials.  Loads are issued in batches of kBatch before any
   // of them is used, so the combine costs a few memory round trips instead of
   // one per partial and per logit; sums keep the order c = 0, 1, ..., S - 1.
+  // The partials' maxima and sums (S <= 64 each) live in s_o, free once this
+  // workgroup's own partial is published: the kernel takes no more LDS than
+  // the fused one, as the launch-time LDS check assumes.
+  static_assert(NG * D >= 128, "s_o holds the partials' maxima and sums");
+  float* s_pm = &s_o[0][0];
+  float* s_pl = s_pm + 64;
   constexpr int kBatch = 8;
   const float* up = sp.partials + (size_t)unit * S * (D + 2);
   // The rows the admission writes (still intact: only this workgroup writes

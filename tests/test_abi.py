@@ -225,6 +225,19 @@ def test_lds_budget_of_large_e4m3_budget():
     assert k2.h2o_destroy(ctx) == B.H2O_OK
 
 
+def test_lds_limit_of_the_e4m3_decode_with_eight_wavefronts():
+    # the single-step kernels keep k + 1 logits in LDS beside their static
+    # arrays; for an E4M3 cache, d = 128 and 8 wavefronts the largest budget
+    # that fits is k = 7895 (the GPU tests run the split decode there)
+    base = dict(head_dim=128, kv_dtype=B.H2O_BF16, cache_dtype=B.H2O_CACHE_E4M3, decode_waves=8,
+                decode_split=1)
+    st, ctx = k2.h2o_create(cfg(recent=3948, heavy=3947, **base), state(ks=FAKE, vs=FAKE))
+    assert st == B.H2O_OK and ctx
+    assert k2.h2o_destroy(ctx) == B.H2O_OK
+    st, ctx = k2.h2o_create(cfg(recent=3948, heavy=3948, **base), state(ks=FAKE, vs=FAKE))
+    assert st == B.H2O_ERR_UNSUPPORTED and ctx is None
+
+
 def test_launch_shape_reports_the_automatic_choices():
     # small budgets never split (each share would keep fewer than 256 rows) and
     # the automatic wave count fills about four wavefronts per SIMD

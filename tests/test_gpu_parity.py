@@ -218,6 +218,17 @@ def test_calls_are_ordered_on_the_callers_stream():
         assert torch.equal(a, b)
 
 
+# ---- the split decode at the LDS limit ------------------------------------------------------
+
+def test_split_decode_at_the_lds_limit():
+    """E4M3 cache with 8 wavefronts per workgroup at k = 7895, the largest
+    budget the create-time LDS check accepts there: the split kernel must take
+    no more LDS than the fused one, so its launches run and match the oracle."""
+    wl = Workload(112, "lds_limit_e4m3", 1, 2, 128, 7950, 4, 3948, 3947, "bf16", "zipf", zipf_alpha=1.1)
+    assert wl.k == 7895
+    run_workload(wl, wl.units, wl.steps, decode_waves=8, decode_split=2, cache="e4m3", kv_every=2)
+
+
 # ---- more units than the device holds at once ----------------------------------------------
 
 MANY_UNITS = Workload(111, "many_units_bf16_d64", 128, 64, 64, 40, 10, 8, 8, "bf16", "fraction",
