@@ -473,9 +473,25 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
     const int j = tid + i * NT;
     if (j < v.n_live) ns_pf[i] = update(j, ns_pf[i], sc_pf[i], ps_pf[i]);
   }
-  for (int j = tid + PF * NT; j < v.n_live; j += NT) {
-    const int s = v.slot_of(j);
-    update(j, s_logit[j], u.score[s], v.is_cand(s) ? u.pos[s] : 0);
+  // Slots past the prefetched ones (budgets above PF * NT): their scores and
+  // positions are loaded kRest at a time before any is used, one memory round
+  // trip per batch instead of per slot (the argmin over unique keys does not
+  // depend on the order).
+  constexpr int kRest = 8;
+  for (int j0 = tid + PF * NT; j0 < v.n_live; j0 += kRest * NT) {
+    float old[kRest];
+    int ps[kRest];
+#pragma unroll
+    for (int i = 0; i < kRest; ++i) {
+      const int s = v.slot_of(min(j0 + i * NT, v.n_live - 1));
+      old[i] = u.score[s];
+      ps[i] = u.pos[s];  // used for candidates only
+    }
+#pragma unroll
+    for (int i = 0; i < kRest; ++i) {
+      const int j = j0 + i * NT;
+      if (j < v.n_live) update(j, s_logit[j], old[i], ps[i]);
+    }
   }
 
   unsigned long long vkey = ~0ull;
