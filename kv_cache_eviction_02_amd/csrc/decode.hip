@@ -980,7 +980,7 @@ int decode_split_auto(int units, int waves, int k, int cus) {
   // One workgroup per unit, unless the units leave compute units idle, the
   // budget is at least kMinK and each share still streams at least kMinRows
   // rows.  Measured on MI355X (32 units, 8 wavefronts per workgroup): 8 shares
-  // of 512 or 1024 rows ran 2.6x and 2.8x faster than one workgroup per unit,
+  // of 512 or 1024 rows ran 2.6x and 3.0x faster than one workgroup per unit,
   // 4 shares of 256 rows 1.24x and 3 shares of 256 rows 1.07x; 2 shares of 256
   // rows (k = 512) and shares of 128 rows lost, the publication round trips
   // (store acknowledgement, arrival count, reads of the partials) costing more
