@@ -387,6 +387,106 @@ def test_e4m3_cache_equals_exact_cache_when_rows_are_representable():
         np.testing.assert_array_equal(a.out, b.out)
 
 
+def torch_e4m3_stored_row(x):
+    """The row an E4M3 cache holds for input row x, built without the oracle:
+    the format the library stores (codes of x * (448 / amax) in float32, row
+    scale amax / 448; a zero row stays zero) with torch's own float8_e4m3fn
+    rounding, read back in float64."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.abs(x).max())
+    if amax == 0:
+        return np.zeros(x.shape)
+    y = (x * (np.float32(448.0) / amax)).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn)
+    return codes.to(torch.float64).numpy() * np.float64(amax / np.float32(448.0))
+
+
+def test_e4m3_cache_off_grid_rows_attend_stored_members_and_exact_token():
+    """Rows off the E4M3 grid with a budget covering the whole sequence: every
+    decode step's output is the library attention (torch SDPA, float64) over
+    the stored (dequantized) rows of the cached positions plus the decoded
+    token's exact row, and the final scores are the prompt's exact column sums
+    plus the column sums of those steps' weights (summary, "What to notice when
+    reading": H2O composes with quantization of the cached rows).  The two
+    other readings (every row exact; the token attending with its stored row)
+    give outputs at least a thousand times the tolerance away at every step, so
+    either mistake fails here."""
+    P, T, d = 10, 14, 16
+    N = P + T
+    Q, K, V = random_qkv(N, d, seed=31, spread=1.5)
+    K = K.astype(np.float32).astype(np.float64)   # float32 inputs, as the library takes them
+    V = V.astype(np.float32).astype(np.float64)
+    scale = 1 / np.sqrt(d)
+    seeded, c, steps = run_trace(Q, K, V, P, T, 4, 30, scale, cache="e4m3")
+    Ks = np.array([torch_e4m3_stored_row(row) for row in K])
+    Vs = np.array([torch_e4m3_stored_row(row) for row in V])
+    assert np.abs(Ks - K).max() > 1e-3            # the rows really are off the grid
+
+    A_prompt = sdpa(Q[:P], K[:P], np.eye(P), scale, causal=True)
+    score = np.zeros(N)
+    score[:P] = A_prompt.sum(0)
+    for s, res in enumerate(steps):
+        t = P + s
+        assert res.evicted is None
+        Kt = np.vstack([Ks[:t], K[t:t + 1]])
+        Vt = np.vstack([Vs[:t], V[t:t + 1]])
+        ref = sdpa(Q[t:t + 1], Kt, Vt, scale)[0]
+        np.testing.assert_allclose(res.out, ref, rtol=1e-12, atol=1e-13)
+        w = sdpa(Q[t:t + 1], Kt, np.eye(t + 1), scale)[0]
+        score[:t + 1] += w
+        # the other readings are clearly different answers
+        all_exact = sdpa(Q[t:t + 1], K[:t + 1], V[:t + 1], scale)[0]
+        token_stored = sdpa(Q[t:t + 1], Ks[:t + 1], Vs[:t + 1], scale)[0]
+        assert np.abs(all_exact - ref).max() > 1e-9 and np.abs(token_stored - ref).max() > 1e-9
+    final = steps[-1].members
+    assert sorted(final) == list(range(N))
+    np.testing.assert_allclose([final[j] for j in range(N)], score, rtol=1e-12, atol=1e-13)
+
+
+def test_e4m3_cache_stored_rows_decide_the_victim():
+    """Hand-built full cache (r = 1: every member is a candidate) whose two
+    lowest scores are separated so that only the stated reading evicts position
+    0: the members attend with their stored E4M3 rows and the decoded token with
+    its exact row.  Attending with the members' exact rows, or with the token's
+    stored row, moves the weight enough to evict position 1 instead."""
+    d, t, r, h = 2, 3, 1, 2
+    scale = 1.0
+    q = np.array([0.0, 10.0])
+    # position 0 and the token are off the grid (0.3 * 448 = 134.4 is stored as
+    # 128); position 1 (0.25 * 448 = 112) and position 2 are on it
+    K = {0: np.array([1.0, 0.3]), 1: np.array([1.0, 0.25]), 2: np.array([1.0, 0.0]),
+         3: np.array([1.0, 0.3])}
+    V = {j: np.array([float(j), 1.0]) for j in K}
+    Ks = {j: torch_e4m3_stored_row(K[j]) for j in K}
+    Vs = {j: torch_e4m3_stored_row(V[j]) for j in V}
+    assert abs(Ks[0][1] - 128 / 448) < 1e-7 and abs(Ks[1][1] - 0.25) < 1e-7
+
+    def weights(k_members, k_token):
+        rows = np.vstack([k_members[j] for j in (0, 1, 2)] + [k_token])
+        return sdpa(q[None], rows, np.eye(4), scale)[0]
+    w_read = weights(Ks, K[3])               # the stated reading
+    w_exact = weights(K, K[3])               # members exact
+    w_tok = weights(Ks, Ks[3])               # token stored
+    th = {name: w[0] - w[1] for name, w in (("read", w_read), ("exact", w_exact), ("tok", w_tok))}
+    # position 0 is evicted iff s1 - s0 > w0 - w1; both other readings need a larger gap
+    assert th["exact"] > th["read"] and th["tok"] > th["read"]
+    gap = th["read"] + 0.5 * (min(th["exact"], th["tok"]) - th["read"])
+    members = {0: 1.0, 1: 1.0 + gap, 2: 50.0}
+    Kc = {j: dequant for j, dequant in Ks.items()}
+    Vc = {j: dequant for j, dequant in Vs.items()}
+    from oracle import dequantize_row_e4m3, quantize_row_e4m3
+    for j in K:   # the oracle's own quantizer stores the same rows
+        np.testing.assert_array_equal(dequantize_row_e4m3(*quantize_row_e4m3(K[j])), Ks[j])
+    res = decode_step(members, t, q, K, V, r, h, scale, Kc, Vc)
+    assert res.evicted == 0
+    np.testing.assert_allclose([res.weights[j] for j in (0, 1, 2, 3)], w_read, rtol=1e-12, atol=1e-15)
+    # the same step under each other reading evicts position 1
+    assert decode_step(members, t, q, K, V, r, h, scale).evicted == 1
+    Kt = dict(Kc)
+    Kt[3] = Ks[3]
+    assert decode_step(members, t, q, Kt, V, r, h, scale, Kc, Vc).evicted == 1
+
+
 def test_e4m3_cache_keeps_definition_4_3():
     wl, Q, K, V = c1_unit(0)
     seeded, _, steps = run_trace(Q, K, V, wl.prompt, wl.steps, wl.recent, wl.heavy, wl.scale,
