@@ -89,13 +89,13 @@ def traffic_for(wl_name, waves, cache="input"):
 # ---- CPU baseline: the oracle on the host cores (runs before any GPU use) -------
 
 def _oracle_worker(args):
-    wl_name, prompt, recent, heavy, policy, units, steps = args
+    wl_name, prompt, recent, heavy, policy, units, steps, blas_threads = args
     import dataclasses as dc
     from threadpoolctl import threadpool_limits
     from oracle import decode_step, prefill
     from synth import WORKLOADS as W, gen
     wl = dc.replace(W[wl_name], prompt=prompt, recent=recent, heavy=heavy)
-    with threadpool_limits(1):
+    with threadpool_limits(blas_threads):
         data = []
         pre_s = 0.0
         for u in units:
@@ -114,20 +114,8 @@ def _oracle_worker(args):
     return len(units) * steps, dt, len(units), pre_s
 
 
-def cpu_baseline(wl, units_per_worker, steps, policy="h2o"):
-    import multiprocessing as mp
-    workers = min(16, len(os.sched_getaffinity(0)))
-    stride = max(1, wl.units // (workers * units_per_worker))
-    chosen = list(range(0, wl.units, stride))[:workers * units_per_worker]
-    jobs = [(wl.name, wl.prompt, wl.recent, wl.heavy, policy, chosen[i::workers], steps)
-            for i in range(workers)]
-    jobs = [j for j in jobs if j[5]]
-    with mp.get_context("fork").Pool(len(jobs)) as pool:
-        res = pool.map(_oracle_worker, jobs)
-    unit_steps_per_s = sum(n / dt for n, dt, _, _ in res)
-    cpu_work = sum(dt for _, dt, _, _ in res)
-    # oracle prefill: per-unit time on one core, scaled to the whole batch over the workers
-    pre_unit_s = sum(ps for _, _, _, ps in res) / sum(nu for _, _, nu, _ in res)
+def host_cpu():
+    """(cores this process may run on, CPU model name from /proc/cpuinfo)."""
     model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -136,17 +124,83 @@ def cpu_baseline(wl, units_per_worker, steps, policy="h2o"):
                 break
     except OSError:
         pass
+    return len(os.sched_getaffinity(0)), model
+
+
+def cpu_baseline(wl, units_per_worker, steps, policy="h2o"):
+    """The oracle on every core of the host: at most 16 worker processes (one
+    per unit sample share), each with host_cores // workers BLAS threads."""
+    import multiprocessing as mp
+    host_cores, model = host_cpu()
+    workers = min(16, host_cores)
+    blas = max(1, host_cores // workers)
+    stride = max(1, wl.units // (workers * units_per_worker))
+    chosen = list(range(0, wl.units, stride))[:workers * units_per_worker]
+    jobs = [(wl.name, wl.prompt, wl.recent, wl.heavy, policy, chosen[i::workers], steps, blas)
+            for i in range(workers)]
+    jobs = [j for j in jobs if j[5]]
+    with mp.get_context("fork").Pool(len(jobs)) as pool:
+        res = pool.map(_oracle_worker, jobs)
+    unit_steps_per_s = sum(n / dt for n, dt, _, _ in res)
+    cpu_work = sum(dt for _, dt, _, _ in res)
+    # oracle prefill: per-unit time on one worker, scaled to the whole batch over the workers
+    pre_unit_s = sum(ps for _, _, _, ps in res) / sum(nu for _, _, nu, _ in res)
     return {
         "value": unit_steps_per_s / wl.units,
         "unit": "steps/s",
-        "cores": len(jobs),
+        "cores": len(jobs) * blas,
         "kind": "oracle",
+        "host_cores": host_cores,
+        "processes": len(jobs),
+        "blas_threads_per_process": blas,
+        "cpu_model": model,
         "prefill_s": pre_unit_s * wl.units / len(jobs),
         "sample": (f"{len(chosen)} of {wl.units} (batch, head) units x {steps} decode steps "
-                   f"after an untimed oracle prefill, float64 numpy, {len(jobs)} processes with one "
-                   f"BLAS thread each; {cpu_work:.1f} s of CPU time; rate scaled to whole-batch "
-                   f"steps/s; host CPU: {model}"),
+                   f"after an untimed oracle prefill, float64 numpy, {len(jobs)} processes with "
+                   f"{blas} BLAS thread(s) each on {host_cores} host cores; {cpu_work:.1f} s of "
+                   f"CPU time; rate scaled to whole-batch steps/s; host CPU: {model}"),
     }
+
+
+def rocminfo_record():
+    """Fields of the first gfx agent in rocminfo's listing (name, clocks and unit
+    counts), read before any GPU use in this process; {} when unavailable."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return {}
+    keys = {"Marketing Name": "marketing_name", "Max Clock Freq. (MHz)": "max_clock_mhz",
+            "Compute Unit": "compute_units", "SIMDs per CU": "simds_per_cu",
+            "Wavefront Size": "wavefront_size", "Max Waves Per CU": "max_waves_per_cu",
+            "Shader Engines": "shader_engines"}
+    for agent in txt.split("Agent ")[1:]:
+        if "gfx9" not in agent or "Device Type:" not in agent or "GPU" not in agent.split("Device Type:")[1][:20]:
+            continue
+        rec = {}
+        for line in agent.splitlines():
+            k, _, v = line.strip().partition(":")
+            if k.strip() in keys and keys[k.strip()] not in rec:
+                v = v.strip().split("(")[0].strip()
+                rec[keys[k.strip()]] = int(v) if v.isdigit() else v
+        return rec
+    return {}
+
+
+def smi_clocks():
+    """Current and top shader and memory clocks reported by rocm-smi (MHz), or {}."""
+    import re
+    import subprocess
+    try:
+        txt = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return {}
+    rec = {}
+    for name, key in (("sclk", "sclk_mhz"), ("mclk", "mclk_mhz"), ("fclk", "fclk_mhz")):
+        m = re.search(rf"{name} clock level:\s*\d+:\s*\(?(\d+)\s*Mhz", txt, re.I)
+        if m:
+            rec[key] = int(m.group(1))
+    return rec
 
 
 # ---- GPU -----------------------------------------------------------------------
@@ -405,6 +459,10 @@ def main():
 
     if args.cache == "e4m3" and wl.kv_dtype != "bf16":
         sys.exit("an E4M3 cache takes bf16 inputs")
+    # device listing and clocks from the ROCm tools, in child processes, before this
+    # process touches the GPU
+    agent = rocminfo_record()
+    clocks = smi_clocks()
     g = run_gpu(wl, steps, warmup, args.decode_waves, args.copy_calibration_mib, args.single_step_calls,
                 args.decode_split, args.cache, args.policy, not args.no_streaming)
     ms_per_step = g["region_ms"] / steps
@@ -490,7 +548,7 @@ def main():
             "workgroups": g["read_best"][1],
             "decode_frac_of_ceiling": achieved / g["read_best"][0]},
         "cpu_baseline": cpu,
-        "device": g["device"],
+        "device": {**g["device"], "rocminfo": agent, "clocks": clocks},
     }
     print(json.dumps(line), flush=True)
 

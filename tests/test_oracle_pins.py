@@ -327,6 +327,32 @@ def test_tiny_trace_matches_recorded_trajectory():
         assert sorted(steps[-1].members) == u["final_members"]
 
 
+def test_stream_trace_matches_recorded_trajectory_and_evicts_heavy_members():
+    """The recorded long-stream trajectory (first 2000 steps, heads 0-3) is the
+    oracle's own; here its first 400 steps of head 0 are replayed.  Many of its
+    evictions remove a heavy member, not the position leaving the window, so it
+    separates H2O from Local and from a static Top-K, whose victim is always
+    t - recent."""
+    import json
+    import os
+    from oracle import prefill as oracle_prefill
+    path = os.path.join(os.path.dirname(__file__), "golden", "llama7b_stream_trace.json")
+    rec = json.load(open(path))
+    wl = WORKLOADS["llama7b_stream"]
+    P, r, h = wl.prompt, wl.recent, wl.heavy
+    for u in rec["units"]:
+        assert u["heavy_evictions"] == sum(e != P + s - r for s, e in enumerate(u["evicted"])) > 40
+    u = rec["units"][0]
+    n = 400
+    Q, K, V = gen.unit_values(wl, 0, u["head"], 0, P + n)
+    members, _ = oracle_prefill(Q[:P], K[:P], r, h, wl.scale)
+    assert sorted(members) == u["prefill_kept"]
+    for s in range(n):
+        res = decode_step(members, P + s, Q[P + s], K, V, r, h, wl.scale)
+        assert res.evicted == u["evicted"][s], s
+        members = res.members
+
+
 # --- E4M3 cache rows -------------------------------------------------------------
 
 def test_e4m3_encode_matches_torch_float8_e4m3fn():
