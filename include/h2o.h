@@ -64,7 +64,8 @@ typedef enum {
   H2O_ERR_UNSUPPORTED = 2, /* head_dim not in {64, 96, 128}, k above the kernel limit */
   H2O_ERR_STATE = 3,       /* call order: decode before any prefill/adopted state, position overflow */
   H2O_ERR_OOM = 4,         /* scratch allocation failed */
-  H2O_ERR_HIP = 5          /* a HIP runtime call or launch failed */
+  H2O_ERR_HIP = 5,         /* a HIP runtime call or launch failed */
+  H2O_ERR_TOO_LARGE = 6    /* h2o_prefill_no_alloc: needs more than H2O_NO_ALLOC_SCRATCH_BYTES */
 } h2o_status;
 
 typedef enum { H2O_F32 = 0, H2O_BF16 = 1 } h2o_dtype;
@@ -220,6 +221,29 @@ h2o_status h2o_query(const h2o_ctx* ctx, int32_t* next_pos, int32_t* n_live);
  * workgroups per (batch, head) unit (1 = no split), after the automatic
  * choices and the LDS check.  Either pointer may be NULL. */
 h2o_status h2o_launch_shape(const h2o_ctx* ctx, int32_t* decode_waves, int32_t* decode_split);
+
+/* Scratch bytes h2o_prefill_no_alloc may use on a device (32 MiB). */
+#define H2O_NO_ALLOC_SCRATCH_BYTES (32u << 20)
+
+/* h2o_prefill_with_output for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops that must not call hipMalloc, and
+ * harnesses that forbid it.  It allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine): the row statistics and column sums go to a
+ * fixed array of H2O_NO_ALLOC_SCRATCH_BYTES in the library's code object,
+ * which every device the library runs on holds until the process ends, instead
+ * of the ctx's scratch.  The ctx may therefore be created with max_prompt = 0
+ * (then h2o_create allocates no device memory either, unless the decode is
+ * split).  Same kernels and same results as h2o_prefill_with_output; out ==
+ * NULL is h2o_prefill.  Needs 2 * batch * heads * round_up(prompt_len, 16) * 4
+ * bytes of that array: a larger call returns H2O_ERR_TOO_LARGE before anything
+ * is enqueued, as do the errors of h2o_prefill_with_output except that
+ * prompt_len is not bounded by max_prompt (1 <= prompt_len <= H2O_MAX_PROMPT).
+ * All calls on one device share its array and leave their contents in it:
+ * calls that overlap on one device (other streams, threads or contexts) race,
+ * so the caller must order them.  The first call on a device asks the runtime
+ * for the array's address on that device (H2O_ERR_HIP if that fails). */
+h2o_status h2o_prefill_no_alloc(h2o_ctx* ctx, const void* q, const void* k, const void* v,
+                                int32_t prompt_len, float* out, void* stream);
 
 /* Free the scratch and the ctx.  NULL-safe.  Never frees caller buffers.  The
  * caller must make sure no enqueued work still uses the ctx's scratch. */

@@ -11,7 +11,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libh2o.so")
 
-H2O_OK, H2O_ERR_INVALID, H2O_ERR_UNSUPPORTED, H2O_ERR_STATE, H2O_ERR_OOM, H2O_ERR_HIP = range(6)
+H2O_OK, H2O_ERR_INVALID, H2O_ERR_UNSUPPORTED, H2O_ERR_STATE, H2O_ERR_OOM, H2O_ERR_HIP, H2O_ERR_TOO_LARGE = range(7)
 H2O_F32, H2O_BF16 = 0, 1
 H2O_CACHE_INPUT, H2O_CACHE_E4M3 = 0, 1
 H2O_POLICY_H2O, H2O_POLICY_STATIC, H2O_POLICY_NAIVE = 0, 1, 2
@@ -20,6 +20,7 @@ H2O_STEPS_AUTO, H2O_STEPS_PER_STEP, H2O_STEPS_PERSISTENT = 0, 1, 2
 STEPS_MODES = {"auto": H2O_STEPS_AUTO, "per_step": H2O_STEPS_PER_STEP, "persistent": H2O_STEPS_PERSISTENT}
 H2O_MAX_K = 8192
 H2O_MAX_PROMPT = 1 << 28
+H2O_NO_ALLOC_SCRATCH_BYTES = 32 << 20
 
 STATUS_NAMES = {
     H2O_OK: "H2O_OK",
@@ -28,6 +29,7 @@ STATUS_NAMES = {
     H2O_ERR_STATE: "H2O_ERR_STATE",
     H2O_ERR_OOM: "H2O_ERR_OOM",
     H2O_ERR_HIP: "H2O_ERR_HIP",
+    H2O_ERR_TOO_LARGE: "H2O_ERR_TOO_LARGE",
 }
 
 
@@ -87,6 +89,8 @@ def load_library(path=LIB_PATH):
     lib.h2o_prefill.restype = ctypes.c_int
     lib.h2o_prefill_with_output.argtypes = [vp, vp, vp, vp, i32, vp, vp]
     lib.h2o_prefill_with_output.restype = ctypes.c_int
+    lib.h2o_prefill_no_alloc.argtypes = [vp, vp, vp, vp, i32, vp, vp]
+    lib.h2o_prefill_no_alloc.restype = ctypes.c_int
     lib.h2o_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.h2o_decode_step.restype = ctypes.c_int
     lib.h2o_decode_steps.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
@@ -127,6 +131,10 @@ def h2o_prefill(ctx, q, k, v, prompt_len, stream):
 
 def h2o_prefill_with_output(ctx, q, k, v, prompt_len, out, stream):
     return load_library().h2o_prefill_with_output(ctx, q, k, v, prompt_len, out, stream)
+
+
+def h2o_prefill_no_alloc(ctx, q, k, v, prompt_len, out, stream):
+    return load_library().h2o_prefill_no_alloc(ctx, q, k, v, prompt_len, out, stream)
 
 
 def h2o_decode_step(ctx, q, k_new, v_new, out, evicted_pos, stream):
@@ -240,13 +248,20 @@ class H2OCache:
                              f"got {x.dtype} {tuple(x.shape)} on {x.device}")
         return x.data_ptr()
 
-    def prefill(self, q, k, v, output=False, out=None):
+    def prefill(self, q, k, v, output=False, out=None, no_alloc=False):
         """Seed the cache from a prompt [B, H, P, d].  With output=True (or an
         out tensor) also returns the prompt's attention output [B, H, P, d]
-        float32."""
+        float32.  no_alloc=True calls h2o_prefill_no_alloc (its scratch is the
+        library's fixed buffer, not the ctx's)."""
         P = q.shape[2]
         shape = (self.batch, self.heads, P, self.head_dim)
         ptrs = [self._input(x, shape, n) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
+        if no_alloc:
+            if output and out is None:
+                out = self.torch.empty(shape, dtype=self.torch.float32, device=self.device)
+            optr = None if out is None else self._output(out, shape, self.torch.float32, "out")
+            _check(h2o_prefill_no_alloc(self.ctx, *ptrs, P, optr, self._stream()), "h2o_prefill_no_alloc")
+            return out
         if not output and out is None:
             _check(h2o_prefill(self.ctx, *ptrs, P, self._stream()), "h2o_prefill")
             return None

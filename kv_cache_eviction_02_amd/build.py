@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libh2o.so")
-SOURCES = ["h2o_api.cpp", "decode.hip", "prefill.hip"]
+SOURCES = ["h2o_api.cpp", "decode.hip", "prefill.hip", "prefill_no_alloc.hip"]
 PROBE_LIB = os.path.join(PKG, "libh2o_probe.so")
 PROBE_SOURCES = ["read_probe.hip"]
 ARCH = "gfx950"

@@ -10,23 +10,8 @@
 
 #include <new>
 
+#include "ctx.h"
 #include "launch.h"
-
-struct h2o_ctx {
-  h2o_config cfg;
-  h2o_state st;
-  int32_t k;
-  int32_t waves;
-  float scale_log2;
-  int32_t t;        // absolute position of the next token to decode
-  int32_t n_live;   // live slots per unit
-  bool has_state;
-  int32_t stride;   // scratch row stride (floats)
-  float* scratch;   // 2 * units * stride floats: row log-sum-exp, column sums
-  h2o::SplitScratch split;  // split decode scratch (split.splits < 2: unused)
-  void* split_mem;
-  int64_t multi_capacity;   // units the multi-step kernel keeps resident at once; -1 = not asked yet
-};
 
 namespace {
 
@@ -158,12 +143,32 @@ h2o_status h2o_prefill(h2o_ctx* ctx, const void* q, const void* k, const void* v
 
 h2o_status h2o_prefill_with_output(h2o_ctx* ctx, const void* q, const void* k, const void* v,
                                    int32_t prompt_len, float* out, void* stream) {
+  const h2o_status st = h2o::check_prefill(ctx, q, k, v, prompt_len, out);
+  if (st != H2O_OK) return st;
+  if (prompt_len > ctx->cfg.max_prompt) return H2O_ERR_INVALID;
+  const size_t units = (size_t)ctx->cfg.batch * ctx->cfg.heads;
+  return h2o::run_prefill(ctx, q, k, v, prompt_len, out, ctx->scratch, ctx->scratch + units * ctx->stride,
+                          ctx->stride, stream);
+}
+
+}  // extern "C"
+
+namespace h2o {
+
+h2o_status check_prefill(const h2o_ctx* ctx, const void* q, const void* k, const void* v, int32_t prompt_len,
+                         const float* out) {
   if (!ctx || !q || !k || !v) return H2O_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (out && !aligned16(out))) return H2O_ERR_INVALID;
-  if (prompt_len < 1 || prompt_len > ctx->cfg.max_prompt) return H2O_ERR_INVALID;
+  if (prompt_len < 1 || prompt_len > H2O_MAX_PROMPT) return H2O_ERR_INVALID;
+  const int64_t units = (int64_t)ctx->cfg.batch * ctx->cfg.heads;
+  if ((int64_t)((prompt_len + 63) / 64) * units > INT32_MAX) return H2O_ERR_INVALID;
+  return H2O_OK;
+}
+
+h2o_status run_prefill(h2o_ctx* ctx, const void* q, const void* k, const void* v, int32_t prompt_len, float* out,
+                       float* row_lse, float* colsum, int32_t stride, void* stream) {
   const size_t units = (size_t)ctx->cfg.batch * ctx->cfg.heads;
-  if ((int64_t)((prompt_len + 63) / 64) * (int64_t)units > INT32_MAX) return H2O_ERR_INVALID;
-  h2o::PrefillArgs a;
+  PrefillArgs a;
   a.pq = q;
   a.pk = k;
   a.pv = v;
@@ -173,19 +178,19 @@ h2o_status h2o_prefill_with_output(h2o_ctx* ctx, const void* q, const void* k, c
   a.pos = ctx->st.pos;
   a.k_scale = ctx->st.k_scale;
   a.v_scale = ctx->st.v_scale;
-  a.row_lse = ctx->scratch;
-  a.colsum = ctx->scratch + units * ctx->stride;
+  a.row_lse = row_lse;
+  a.colsum = colsum;
   a.out = out;
   a.units = (int32_t)units;
-  a.stride = ctx->stride;
+  a.stride = stride;
   a.P = prompt_len;
   a.k = ctx->k;
   a.r = ctx->cfg.recent;
   a.h = ctx->cfg.heavy;
   a.scale_log2 = ctx->scale_log2;
   a.last_row_only = ctx->cfg.policy == H2O_POLICY_NAIVE;
-  const hipError_t e = h2o::launch_prefill(a, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype,
-                                           ctx->cfg.head_dim, (hipStream_t)stream);
+  const hipError_t e = launch_prefill(a, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype, ctx->cfg.head_dim,
+                                      (hipStream_t)stream);
   if (e != hipSuccess) return from_hip(e);
   ctx->t = prompt_len;
   ctx->n_live = prompt_len < ctx->k ? prompt_len : ctx->k;
@@ -193,7 +198,7 @@ h2o_status h2o_prefill_with_output(h2o_ctx* ctx, const void* q, const void* k, c
   return H2O_OK;
 }
 
-}  // extern "C"
+}  // namespace h2o
 
 namespace {
 
@@ -343,6 +348,7 @@ const char* h2o_status_string(h2o_status status) {
     case H2O_ERR_STATE: return "invalid call order or position overflow";
     case H2O_ERR_OOM: return "out of device memory";
     case H2O_ERR_HIP: return "HIP runtime error";
+    case H2O_ERR_TOO_LARGE: return "needs more scratch than the fixed no-allocation buffer holds";
   }
   return "unknown status";
 }

@@ -37,7 +37,7 @@ def state(k=FAKE, v=FAKE, s=FAKE, p=FAKE, ks=None, vs=None):
 def test_library_exports_every_header_function():
     lib = B.load_library()
     names = header_functions()
-    assert names == sorted(["h2o_create", "h2o_prefill", "h2o_prefill_with_output",
+    assert names == sorted(["h2o_create", "h2o_prefill", "h2o_prefill_with_output", "h2o_prefill_no_alloc",
                             "h2o_decode_step", "h2o_decode_steps",
                             "h2o_query", "h2o_launch_shape", "h2o_destroy", "h2o_status_string"])
     for n in names:
@@ -78,7 +78,7 @@ int main(void) {
 
 
 def test_status_strings():
-    for code in range(6):
+    for code in range(7):
         assert k2.status_string(code)
     assert k2.status_string(99) == "unknown status"
 
@@ -153,6 +153,32 @@ def test_call_order_and_argument_checks_without_device_work():
     assert k2.h2o_destroy(None) == B.H2O_OK
     assert B.load_library().h2o_query(None, None, None) == B.H2O_ERR_INVALID
     assert B.load_library().h2o_launch_shape(None, None, None) == B.H2O_ERR_INVALID
+
+
+def test_no_alloc_prefill_checks_without_device_work():
+    """h2o_prefill_no_alloc validates like h2o_prefill_with_output, except that
+    max_prompt does not bound it, and refuses a prompt whose row statistics and
+    column sums would not fit its fixed buffer, before any HIP call."""
+    assert B.H2O_NO_ALLOC_SCRATCH_BYTES == 32 << 20
+    st, ctx = k2.h2o_create(cfg(batch=64, heads=56), state())   # max_prompt = 0: nothing allocated
+    assert st == B.H2O_OK
+    try:
+        f = k2.h2o_prefill_no_alloc
+        assert f(ctx, FAKE, FAKE, FAKE, 0, None, None) == B.H2O_ERR_INVALID
+        assert f(ctx, 0, FAKE, FAKE, 16, None, None) == B.H2O_ERR_INVALID
+        assert f(ctx, FAKE, FAKE, FAKE + 8, 16, None, None) == B.H2O_ERR_INVALID
+        assert f(ctx, FAKE, FAKE, FAKE, 16, FAKE + 4, None) == B.H2O_ERR_INVALID
+        assert f(ctx, FAKE, FAKE, FAKE, (1 << 28) + 1, None, None) == B.H2O_ERR_INVALID
+        # 2 * 3584 units * round_up(P, 16) floats must fit 32 MiB: P = 1168 fits, 1169 does not
+        units = 64 * 56
+        assert 2 * units * 1168 * 4 <= 32 << 20 < 2 * units * 1184 * 4
+        assert f(ctx, FAKE, FAKE, FAKE, 1169, None, None) == B.H2O_ERR_TOO_LARGE
+        assert f(ctx, FAKE, FAKE, FAKE, 1 << 20, FAKE, None) == B.H2O_ERR_TOO_LARGE
+        assert k2.h2o_query(ctx) == (B.H2O_OK, 0, 0)
+        assert "no-allocation" in k2.status_string(B.H2O_ERR_TOO_LARGE)
+    finally:
+        assert k2.h2o_destroy(ctx) == B.H2O_OK
+    assert k2.h2o_prefill_no_alloc(None, FAKE, FAKE, FAKE, 16, None, None) == B.H2O_ERR_INVALID
 
 
 def test_adopted_state_counters():
