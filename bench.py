@@ -340,7 +340,7 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     r1.record(stream)
     torch.cuda.synchronize()
     region_ms = r0.elapsed_time(r1)
-    stream_ms = None
+    stream_ms = resident_ms = None
     if streaming and not single_calls:
         # the same steps as one persistent launch (known tokens, as in a long-stream run);
         # h2o_decode_steps picks it by itself for small batches (steps_mode "auto")
@@ -358,6 +358,22 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
         torch.cuda.synchronize()
         stream_ms = r0.elapsed_time(r1)
         pc.close()
+        # the same steps with every unit's rows held in LDS across them, when they fit
+        rc = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy, wl.prompt, dtype,
+                      wl.scale, device=dev, decode_waves=waves, decode_split=split, cache=cache_kind,
+                      policy=policy, steps_mode="resident")
+        rc.prefill(*prompt_keep)
+        if warmup:
+            rc.steps(dq[:warmup], dk[:warmup], dv[:warmup])
+        if steps > 1 and rc.steps_launch(steps) == "resident":
+            torch.cuda.synchronize()
+            r0.record(stream)
+            rc.steps(dq[warmup:warmup + steps], dk[warmup:warmup + steps], dv[warmup:warmup + steps],
+                     out=out_all, evicted=ev_all)
+            r1.record(stream)
+            torch.cuda.synchronize()
+            resident_ms = r0.elapsed_time(r1)
+        rc.close()
     del prompt_keep
     copy_gbs = None
     if not copy_mib:
@@ -396,7 +412,7 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     clock = getattr(props, "clock_rate", None)
     if clock:
         device["clock_mhz"] = clock / 1000
-    return dict(region_ms=region_ms, stream_ms=stream_ms, prefill_ms=prefill_ms, prefill_out_ms=prefill_out_ms,
+    return dict(region_ms=region_ms, stream_ms=stream_ms, resident_ms=resident_ms, prefill_ms=prefill_ms, prefill_out_ms=prefill_out_ms,
                 sdpa_ms=sdpa_ms, read_best=read_best, waves=waves_used, split=split_used, device=device, copy_gbs=copy_gbs)
 
 
@@ -537,6 +553,12 @@ def main():
             "ms_per_step": g["stream_ms"] / steps,
             "achieved": bytes_step * steps / (g["stream_ms"] * 1e-3) / 1e9,
             "frac": bytes_step * steps / (g["stream_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            # the same steps with the rows held in LDS (one launch; none when they do not fit)
+            "resident": None if g["resident_ms"] is None else {
+                "kernel": "decode_resident_kernel",
+                "value": 1e3 * steps / g["resident_ms"],
+                "ms_per_step": g["resident_ms"] / steps,
+            },
         },
         "copy_ceiling": None if g["copy_gbs"] is None else {
             "kind": "device-to-device copy, 2 GiB read + 2 GiB written (torch)",

@@ -38,7 +38,9 @@
  *     stream).  Every call that touches device memory only enqueues work on
  *     `stream` and returns without synchronising.
  *   - All arguments are validated before any HIP call; on an error return the
- *     state buffers and the ctx counters are unchanged.
+ *     state buffers and the ctx counters are unchanged, except when a launch
+ *     of h2o_decode_steps' per-step path fails after earlier steps were
+ *     enqueued: the counters then count those steps (h2o_query).
  *   - A ctx is not thread-safe; calls on one ctx must be serialised by the
  *     caller, and consecutive calls must go to the same stream (or be ordered
  *     by the caller) because each step reads what the previous one wrote.
@@ -101,16 +103,29 @@ typedef enum { H2O_POLICY_H2O = 0, H2O_POLICY_STATIC = 1, H2O_POLICY_NAIVE = 2 }
 
 /* How h2o_decode_steps launches its n steps.  H2O_STEPS_PERSISTENT: one
  * launch carries every (batch, head) unit through all n steps, keeping its
- * scores and positions in LDS between steps; it pays off when a step moves
- * little data (launch and tail latency dominate) and loses to per-step
- * launches with single-wavefront units on large batches.  H2O_STEPS_PER_STEP:
- * one launch per step.  H2O_STEPS_AUTO: persistent when every unit's workgroup
- * fits on the device at once (the runtime's occupancy for the kernel) and
- * either the decode runs several wavefronts per unit or the cached K/V rows
- * of one step total at most 64 MiB; else per step.  Persistent launches also
- * need decode_split = 1 and the unit's 3k + 1 words of LDS; otherwise one
+ * scores and positions in LDS between steps and streaming its K/V rows from
+ * memory at every step; it pays off when a step moves little data (launch and
+ * tail latency dominate) and loses to per-step launches with single-wavefront
+ * units on large batches.  H2O_STEPS_RESIDENT: one launch that also keeps
+ * each unit's K/V rows (and E4M3 row scales) in LDS across the steps, so a
+ * step reads only its new token from memory (the long-stream case: summary,
+ * "Algorithm / figure walkthrough", step 5, memory stays O(k)); it needs a
+ * compute unit per (batch, head) unit and 2k rows plus 3k + 1 words of LDS
+ * within the device's per-workgroup limit (k = 256 at d = 128 in bf16 on
+ * MI355X), else one launch per step is used.  H2O_STEPS_PER_STEP: one launch
+ * per step.  H2O_STEPS_AUTO: resident when it fits and n_steps > 1; else
+ * persistent when every unit's workgroup fits on the device at once (the
+ * runtime's occupancy for the kernel) and either the decode runs several
+ * wavefronts per unit or the cached K/V rows of one step total at most 64 MiB;
+ * else per step.  Persistent and resident launches also need decode_split = 1
+ * and the unit's 3k + 1 words of LDS beside the kernel's own; otherwise one
  * launch per step is used.  Results are bit-identical in every mode. */
-typedef enum { H2O_STEPS_AUTO = 0, H2O_STEPS_PER_STEP = 1, H2O_STEPS_PERSISTENT = 2 } h2o_steps_mode;
+typedef enum {
+  H2O_STEPS_AUTO = 0,
+  H2O_STEPS_PER_STEP = 1,
+  H2O_STEPS_PERSISTENT = 2,
+  H2O_STEPS_RESIDENT = 3
+} h2o_steps_mode;
 
 /* Longest prompt a ctx can be created for (max_prompt). */
 #define H2O_MAX_PROMPT (1 << 28)
@@ -212,6 +227,13 @@ h2o_status h2o_decode_step(h2o_ctx* ctx, const void* q, const void* k_new, const
  * reflect the steps that were enqueued. */
 h2o_status h2o_decode_steps(h2o_ctx* ctx, int32_t n_steps, const void* q, const void* k_new,
                             const void* v_new, float* out, int32_t* evicted_pos, void* stream);
+
+/* How h2o_decode_steps would launch n_steps steps on this ctx now:
+ * *mode = H2O_STEPS_RESIDENT or H2O_STEPS_PERSISTENT (one launch, with or
+ * without the rows held in LDS) or H2O_STEPS_PER_STEP (one launch per step),
+ * after the steps_mode of the config and the device checks it implies.  May
+ * ask the runtime for device attributes (once per ctx); enqueues nothing. */
+h2o_status h2o_steps_launch(h2o_ctx* ctx, int32_t n_steps, int32_t* mode);
 
 /* Host-side counters: position of the next token to decode and number of live
  * slots per unit (the same for every unit).  Either pointer may be NULL. */

@@ -16,8 +16,9 @@ H2O_F32, H2O_BF16 = 0, 1
 H2O_CACHE_INPUT, H2O_CACHE_E4M3 = 0, 1
 H2O_POLICY_H2O, H2O_POLICY_STATIC, H2O_POLICY_NAIVE = 0, 1, 2
 POLICIES = {"h2o": H2O_POLICY_H2O, "static": H2O_POLICY_STATIC, "naive": H2O_POLICY_NAIVE}
-H2O_STEPS_AUTO, H2O_STEPS_PER_STEP, H2O_STEPS_PERSISTENT = 0, 1, 2
-STEPS_MODES = {"auto": H2O_STEPS_AUTO, "per_step": H2O_STEPS_PER_STEP, "persistent": H2O_STEPS_PERSISTENT}
+H2O_STEPS_AUTO, H2O_STEPS_PER_STEP, H2O_STEPS_PERSISTENT, H2O_STEPS_RESIDENT = 0, 1, 2, 3
+STEPS_MODES = {"auto": H2O_STEPS_AUTO, "per_step": H2O_STEPS_PER_STEP, "persistent": H2O_STEPS_PERSISTENT,
+               "resident": H2O_STEPS_RESIDENT}
 H2O_MAX_K = 8192
 H2O_MAX_PROMPT = 1 << 28
 H2O_NO_ALLOC_SCRATCH_BYTES = 32 << 20
@@ -99,6 +100,8 @@ def load_library(path=LIB_PATH):
     lib.h2o_query.restype = ctypes.c_int
     lib.h2o_launch_shape.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.h2o_launch_shape.restype = ctypes.c_int
+    lib.h2o_steps_launch.argtypes = [vp, i32, ctypes.POINTER(i32)]
+    lib.h2o_steps_launch.restype = ctypes.c_int
     lib.h2o_destroy.argtypes = [vp]
     lib.h2o_destroy.restype = ctypes.c_int
     lib.h2o_status_string.argtypes = [ctypes.c_int]
@@ -155,6 +158,12 @@ def h2o_launch_shape(ctx):
     w, s = ctypes.c_int32(), ctypes.c_int32()
     st = load_library().h2o_launch_shape(ctx, ctypes.byref(w), ctypes.byref(s))
     return st, w.value, s.value
+
+
+def h2o_steps_launch(ctx, n_steps):
+    m = ctypes.c_int32()
+    st = load_library().h2o_steps_launch(ctx, n_steps, ctypes.byref(m))
+    return st, m.value
 
 
 def h2o_destroy(ctx):
@@ -310,6 +319,12 @@ class H2OCache:
         st, w, sp = h2o_launch_shape(self.ctx)
         _check(st, "h2o_launch_shape")
         return w, sp
+
+    def steps_launch(self, n_steps):
+        """How steps() would launch n_steps steps now: "resident", "persistent" or "per_step"."""
+        st, m = h2o_steps_launch(self.ctx, n_steps)
+        _check(st, "h2o_steps_launch")
+        return {v: k for k, v in STEPS_MODES.items()}[m]
 
     def close(self):
         if getattr(self, "ctx", None):

@@ -21,6 +21,8 @@ struct h2o_ctx {
   h2o::SplitScratch split;  // split decode scratch (split.splits < 2: unused)
   void* split_mem;
   int64_t multi_capacity;   // units the multi-step kernel keeps resident at once; -1 = not asked yet
+  int32_t cus;              // compute units of the ctx's device; -1 = not asked yet
+  int64_t lds_limit;        // LDS one workgroup may take on the ctx's device; -1 = not asked yet
 };
 
 namespace h2o {

@@ -115,6 +115,11 @@ struct Geo {
 };
 
 constexpr float kLazyMax = 8.f;  // log2 units a row group's running maximum may lag
+// Running maximum of a row group before its first row: finite, so that the
+// weight exp2(lg - m) of a row outside the range (lg = -inf) is 0 without a
+// test, and the first row raises the maximum (its rescale factor exp2(kNoMax -
+// lg) is 0, as it would be from -inf).
+constexpr float kNoMax = -FLT_MAX;
 constexpr int kSelfVictim = -2;  // victim marker: the decoded token itself (r = 0)
 
 // One unit's step as seen by every thread.  With r = 0 there is no ring:
@@ -178,6 +183,53 @@ struct Stash {
   float ring_scale[2];     // E4M3 row scales of the ring row
 };
 
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) u32x4_t lds_v4;
+typedef __attribute__((address_space(3))) float lds_f32;
+
+__device__ inline uint4 lds_load16(const lds_char* p) {
+  const u32x4_t v = *reinterpret_cast<const lds_v4*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline void lds_store16(lds_char* p, const uint4& x) {
+  *reinterpret_cast<lds_v4*>(p) = u32x4_t{x.x, x.y, x.z, x.w};
+}
+
+// The unit's K and V rows (and E4M3 row scales) held in LDS by the resident
+// multi-step kernel: the same [k][row] layout as the state buffers.
+template <typename GG>
+struct ResRows {
+  lds_char* K;
+  lds_char* V;
+  lds_f32* ks;   // E4M3 only
+  lds_f32* vs;
+};
+
+// Inputs of one step (the lane's chunks of q and of the new token's K and V
+// rows), loaded ahead of the step.
+template <typename GG>
+struct StepIn {
+  uint4 q[GG::ICH];
+  uint4 k[GG::ICH];
+  uint4 v[GG::ICH];
+};
+
+template <typename GG>
+__device__ __forceinline__ void load_step_in(const UnitPtrs<GG>& u, int chunk, StepIn<GG>& in) {
+#pragma unroll
+  for (int i = 0; i < GG::ICH; ++i) {
+    in.q[i] = load16(u.q + (chunk * GG::ICH + i) * 16);
+    in.k[i] = load16(u.kn + (chunk * GG::ICH + i) * 16);
+    in.v[i] = load16(u.vn + (chunk * GG::ICH + i) * 16);
+  }
+}
+
+template <typename GG>
+__device__ __forceinline__ void unpack_input(const uint4* c, float* x) {
+#pragma unroll
+  for (int i = 0; i < GG::ICH; ++i) GG::EI::unpack(c[i], x + i * GG::EI::kPer16B);
+}
+
 // Row batches base = lo, lo + NG, ... below hi, with the loads of DEPTH - 1
 // batches in flight while one is consumed.  Loads are issued unconditionally,
 // also for up to DEPTH - 1 batches past hi (the callers' fetch re-reads a valid
@@ -218,10 +270,13 @@ constexpr int stream_depth() { return GG::NT / 64 >= 8 ? 4 : 2; }
 // Loads are unconditional (rows outside the range and idle lanes re-read a
 // valid row and are masked out) so the compiler tracks outstanding loads
 // exactly; the next row batch is in flight while the current one is consumed.
-template <typename GG, int DEPTH = stream_depth<GG>()>
+// With RES the cached rows come from the LDS copy `res` and the new token's
+// rows from `in` (loaded ahead of the step); else both from global memory.
+template <typename GG, int DEPTH = stream_depth<GG>(), bool RES = false>
 __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG>& u, int lo, int hi,
                                             const float* qf, float scale_log2, float* s_logit,
-                                            Stash<GG>* st, float& m, float& lsum, float* o) {
+                                            Stash<GG>* st, float& m, float& lsum, float* o,
+                                            const ResRows<GG>* res = nullptr, const StepIn<GG>* in = nullptr) {
   using EC = typename GG::EC;
   constexpr int EPL = GG::EPL, G = GG::G, RW = GG::RW, NG = GG::NG, LPR = GG::LPR;
   const int lane = threadIdx.x & 63;
@@ -233,15 +288,22 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
   if constexpr (!GG::kQuant) {
     auto fetch = [&](int base, RowBuf& b) {
       const int j = base + grp;
-      const char* kp = u.kn;
-      const char* vp = u.vn;
-      if (j < v.n_live && j < hi) {
-        const size_t off = (size_t)v.slot_of(j) * GG::ROWB;
-        kp = u.K + off;
-        vp = u.V + off;
+      if constexpr (RES) {
+        // LDS row k holds the decoded token; it also stands in past the range
+        const int off = ((j < v.n_live && j < hi) ? v.slot_of(j) : v.k) * GG::ROWB + chunk * 16;
+        b.k = lds_load16(res->K + off);
+        b.v = lds_load16(res->V + off);
+      } else {
+        const char* kp = u.kn;
+        const char* vp = u.vn;
+        if (j < v.n_live && j < hi) {
+          const size_t off = (size_t)v.slot_of(j) * GG::ROWB;
+          kp = u.K + off;
+          vp = u.V + off;
+        }
+        b.k = load16_stream(kp + chunk * 16);
+        b.v = load16_stream(vp + chunk * 16);
       }
-      b.k = load16_stream(kp + chunk * 16);
-      b.v = load16_stream(vp + chunk * 16);
     };
     auto consume = [&](int base, const RowBuf& b) {
       const uint4& kr = b.k;
@@ -257,38 +319,41 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
       const float lg = valid ? d * scale_log2 : -INFINITY;
       if (valid) {
         if (gl == 0) s_logit[j] = lg;
-        if (act) {
-          if (j == v.n_live) {
-            st->self[0][gl] = kr;
-            st->self[1][gl] = vr;
-          } else if (v.ring_live && j == v.ring_slot) {
-            st->ring[0][gl] = kr;
-            st->ring[1][gl] = vr;
+        if constexpr (!RES) {  // the resident rows stay readable in LDS until the admission
+          if (act) {
+            if (j == v.n_live) {
+              st->self[0][gl] = kr;
+              st->self[1][gl] = vr;
+            } else if (v.ring_live && j == v.ring_slot) {
+              st->ring[0][gl] = kr;
+              st->ring[1][gl] = vr;
+            }
           }
         }
       }
       if (lg > m + kLazyMax) {  // rare after the first rows: rescale to the new maximum
-        const float alpha = fast_exp2(m - lg);  // 0 while m is -inf
+        const float alpha = fast_exp2(m - lg);  // 0 while m is kNoMax
         lsum *= alpha;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[e] *= alpha;
         m = lg;
       }
-      if (m > -INFINITY) {
-        const float p = fast_exp2(lg - m);  // 0 for rows outside the range; at most 2^kLazyMax
-        float vf[EPL];
-        EC::unpack(vr, vf);
-        lsum += p;
+      const float p = fast_exp2(lg - m);  // 0 for rows outside the range; at most 2^kLazyMax
+      float vf[EPL];
+      EC::unpack(vr, vf);
+      lsum += p;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vf[e], o[e]);
-      }
+      for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vf[e], o[e]);
     };
     row_pipeline<DEPTH, NG, RowBuf>(lo, hi, fetch, consume);
   } else {
     // The decoded token (exact bf16 row) seeds row group 0 when it is in range.
     if (v.n_live >= lo && v.n_live < hi) {
       float kx[EPL];
-      load_input<GG>(u.kn, chunk, kx);
+      if constexpr (RES)
+        unpack_input<GG>(in->k, kx);
+      else
+        load_input<GG>(u.kn, chunk, kx);
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) d = fmaf(qf[e], kx[e], d);
@@ -297,7 +362,10 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
       if (grp == 0) {
         if (gl == 0) s_logit[v.n_live] = ls;
         float vx[EPL];
-        load_input<GG>(u.vn, chunk, vx);
+        if constexpr (RES)
+          unpack_input<GG>(in->v, vx);
+        else
+          load_input<GG>(u.vn, chunk, vx);
         m = ls;
         lsum = 1.f;
 #pragma unroll
@@ -308,11 +376,19 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
     auto fetch = [&](int base, QuantRowBuf& b) {
       const int j = base + grp;
       const int s = (j < end) ? v.slot_of(j) : 0;  // slot 0 stands in past the end
-      const size_t off = (size_t)s * GG::ROWB;
-      b.k = load16_stream(u.K + off + chunk * 16);
-      b.v = load16_stream(u.V + off + chunk * 16);
-      b.ks = u.ks[s];
-      b.vs = u.vs[s];
+      if constexpr (RES) {
+        const int off = s * GG::ROWB + chunk * 16;
+        b.k = lds_load16(res->K + off);
+        b.v = lds_load16(res->V + off);
+        b.ks = res->ks[s];
+        b.vs = res->vs[s];
+      } else {
+        const size_t off = (size_t)s * GG::ROWB;
+        b.k = load16_stream(u.K + off + chunk * 16);
+        b.v = load16_stream(u.V + off + chunk * 16);
+        b.ks = u.ks[s];
+        b.vs = u.vs[s];
+      }
     };
     auto consume = [&](int base, const QuantRowBuf& b) {
       const uint4& kr = b.k;
@@ -330,33 +406,33 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
       const float lg = valid ? d * ksc * scale_log2 : -INFINITY;
       if (valid) {
         if (gl == 0) s_logit[j] = lg;
-        if (v.ring_live && j == v.ring_slot) {
-          if (act) {
-            st->ring[0][gl] = kr;
-            st->ring[1][gl] = vr;
-          }
-          if (gl == 0) {
-            st->ring_scale[0] = ksc;
-            st->ring_scale[1] = vsc;
+        if constexpr (!RES) {
+          if (v.ring_live && j == v.ring_slot) {
+            if (act) {
+              st->ring[0][gl] = kr;
+              st->ring[1][gl] = vr;
+            }
+            if (gl == 0) {
+              st->ring_scale[0] = ksc;
+              st->ring_scale[1] = vsc;
+            }
           }
         }
       }
       if (lg > m + kLazyMax) {  // rare after the first rows: rescale to the new maximum
-        const float alpha = fast_exp2(m - lg);  // 0 while m is -inf
+        const float alpha = fast_exp2(m - lg);  // 0 while m is kNoMax
         lsum *= alpha;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[e] *= alpha;
         m = lg;
       }
-      if (m > -INFINITY) {
-        const float p = fast_exp2(lg - m);
-        const float pv = p * vsc;
-        float vf[EPL];
-        EC::unpack(vr, vf);
-        lsum += p;
+      const float p = fast_exp2(lg - m);  // 0 for rows outside the range
+      const float pv = p * vsc;
+      float vf[EPL];
+      EC::unpack(vr, vf);
+      lsum += p;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = fmaf(pv, vf[e], o[e]);
-      }
+      for (int e = 0; e < EPL; ++e) o[e] = fmaf(pv, vf[e], o[e]);
     };
     row_pipeline<DEPTH, NG, QuantRowBuf>(lo, end, fetch, consume);
   }
@@ -402,8 +478,9 @@ __device__ __forceinline__ GroupMerge<GG::NG> merge_groups(float m, float lsum, 
 
 // Quantize the decoded token's K and V rows into slot `slot` (E4M3 cache):
 // lanes [0, G) of wave 0 take K, lanes [G, 2G) take V, each lane 16 values.
-template <typename GG>
-__device__ inline void admit_quantized(const UnitPtrs<GG>& u, int slot) {
+// With RES the codes and scales also go to the LDS copy of the rows.
+template <typename GG, bool RES = false>
+__device__ inline void admit_quantized(const UnitPtrs<GG>& u, int slot, const ResRows<GG>* res = nullptr) {
   constexpr int G = GG::G, LPR = GG::LPR, EPL = GG::EPL;
   const int tid = threadIdx.x;
   if (tid >= 2 * G) return;
@@ -417,20 +494,27 @@ __device__ inline void admit_quantized(const UnitPtrs<GG>& u, int slot) {
   for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
   amax = group_max<G>(act ? amax : 0.f);
   char* row = (is_v ? u.V : u.K) + (size_t)slot * GG::ROWB;
-  if (act) store16(row + c * 16, quantize16_e4m3(x, amax));
-  if (c == 0) (is_v ? u.vs : u.ks)[slot] = __fdiv_rn(amax, 448.f);
+  const uint4 codes = quantize16_e4m3(x, amax);
+  const float sc = __fdiv_rn(amax, 448.f);
+  if (act) store16(row + c * 16, codes);
+  if (c == 0) (is_v ? u.vs : u.ks)[slot] = sc;
+  if constexpr (RES) {
+    if (act) lds_store16((is_v ? res->V : res->K) + slot * GG::ROWB + c * 16, codes);
+    if (c == 0) (is_v ? res->vs : res->ks)[slot] = sc;
+  }
 }
 
 // Score update, eviction argmin and admission for one unit, given the exact
 // softmax max M and 1/L.  Logits of rows [0, n_att) are in s_logit; the
 // scores this thread owns were prefetched into sc_pf / ps_pf; the ring row and
 // (unquantized caches) the new token's row are in the LDS stash.
-template <typename GG>
+template <typename GG, bool RES = false>
 __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG>& u, float M,
                                             float invL, float* s_logit, const float* sc_pf,
                                             const int* ps_pf, const Stash<GG>* st,
-                                            unsigned long long* s_key, int* s_victim,
-                                            int32_t* evicted, int unit) {
+                                            unsigned long long* s_key, int* s_slot,
+                                            int32_t* evicted, int unit, const ResRows<GG>* res = nullptr,
+                                            const StepIn<GG>* in = nullptr) {
   constexpr int NT = GG::NT, PF = GG::PF, LPR = GG::LPR, ROWB = GG::ROWB;
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
@@ -494,18 +578,32 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
     }
   }
 
+  // The victim's key and slot: each wavefront's minimum and the slot of the
+  // lane holding it go to LDS, and after one barrier every thread takes the
+  // smallest (keys are unique: positions differ).
   unsigned long long vkey = ~0ull;
+  int victim = v.fixed_victim();
   if (v.full && !argmin) {
-    vkey = (uint32_t)v.fixed_victim_pos();  // s_victim keeps its initial fixed_victim()
+    vkey = (uint32_t)v.fixed_victim_pos();
   } else if (v.full) {
     const unsigned long long w = wave_min_u64(best);
     if (lane == 0) s_key[wave] = w;
+    if (best_slot != -1 && best == w) s_slot[wave] = best_slot;
     __syncthreads();
+    int wi = 0;
+    vkey = s_key[0];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) vkey = s_key[i] < vkey ? s_key[i] : vkey;
-    if (best_slot != -1 && best == vkey) *s_victim = best_slot;
+    for (int i = 1; i < NW; ++i) {
+      const unsigned long long ki = s_key[i];
+      if (ki < vkey) {
+        vkey = ki;
+        wi = i;
+      }
+    }
+    victim = s_slot[wi];
+  } else if (!v.full) {
+    __syncthreads();  // thread 0 reads the updated score of the ring row below
   }
-  __syncthreads();
 
   // dst: where the row leaving the window goes (the victim's heavy slot, or the
   // next free heavy slot while the cache is not yet full; -1 if it is dropped or
@@ -515,12 +613,12 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
   if (v.r > 0) {
     adm = v.ring_slot;
     if (v.full) {
-      if (*s_victim != v.ring_slot) dst = *s_victim;
+      if (victim != v.ring_slot) dst = victim;
     } else if (v.ring_live) {
       dst = v.r + v.n_heavy;
     }
   } else {
-    adm = v.full ? (*s_victim == kSelfVictim ? -1 : *s_victim) : v.n_live;
+    adm = v.full ? (victim == kSelfVictim ? -1 : victim) : v.n_live;
   }
 
   auto write_score = [&](int j, float ns) {
@@ -539,8 +637,17 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
       u.score[dst] = s_logit[v.ring_slot];
       u.pos[dst] = v.t - v.r;
       if constexpr (GG::kQuant) {
-        u.ks[dst] = st->ring_scale[0];
-        u.vs[dst] = st->ring_scale[1];
+        if constexpr (RES) {
+          // read before the token's admission below (same wavefront) replaces them
+          const float rk = res->ks[v.ring_slot], rv = res->vs[v.ring_slot];
+          u.ks[dst] = rk;
+          u.vs[dst] = rv;
+          res->ks[dst] = rk;
+          res->vs[dst] = rv;
+        } else {
+          u.ks[dst] = st->ring_scale[0];
+          u.vs[dst] = st->ring_scale[1];
+        }
       }
     }
     if (adm >= 0) {
@@ -549,16 +656,40 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
     }
     if (evicted) evicted[unit] = v.full ? (int32_t)(uint32_t)vkey : -1;
   }
-  if (tid < LPR && dst >= 0) {
-    store16(u.K + (size_t)dst * ROWB + tid * 16, st->ring[0][tid]);
-    store16(u.V + (size_t)dst * ROWB + tid * 16, st->ring[1][tid]);
-  }
-  if (adm >= 0) {
-    if constexpr (GG::kQuant) {
-      admit_quantized<GG>(u, adm);
-    } else if (tid < LPR) {
-      store16(u.K + (size_t)adm * ROWB + tid * 16, st->self[0][tid]);
-      store16(u.V + (size_t)adm * ROWB + tid * 16, st->self[1][tid]);
+  if constexpr (RES) {
+    // Thread tid < LPR moves chunk tid of the rows: the ring row is read from
+    // LDS before the token replaces it, the token's chunk is the lane's own
+    // step input (lane tid holds chunk tid).
+    if (tid < LPR && dst >= 0) {
+      const uint4 rk = lds_load16(res->K + v.ring_slot * ROWB + tid * 16);
+      const uint4 rv = lds_load16(res->V + v.ring_slot * ROWB + tid * 16);
+      store16(u.K + (size_t)dst * ROWB + tid * 16, rk);
+      store16(u.V + (size_t)dst * ROWB + tid * 16, rv);
+      lds_store16(res->K + dst * ROWB + tid * 16, rk);
+      lds_store16(res->V + dst * ROWB + tid * 16, rv);
+    }
+    if (adm >= 0) {
+      if constexpr (GG::kQuant) {
+        admit_quantized<GG, RES>(u, adm, res);
+      } else if (tid < LPR) {
+        store16(u.K + (size_t)adm * ROWB + tid * 16, in->k[0]);
+        store16(u.V + (size_t)adm * ROWB + tid * 16, in->v[0]);
+        lds_store16(res->K + adm * ROWB + tid * 16, in->k[0]);
+        lds_store16(res->V + adm * ROWB + tid * 16, in->v[0]);
+      }
+    }
+  } else {
+    if (tid < LPR && dst >= 0) {
+      store16(u.K + (size_t)dst * ROWB + tid * 16, st->ring[0][tid]);
+      store16(u.V + (size_t)dst * ROWB + tid * 16, st->ring[1][tid]);
+    }
+    if (adm >= 0) {
+      if constexpr (GG::kQuant) {
+        admit_quantized<GG>(u, adm);
+      } else if (tid < LPR) {
+        store16(u.K + (size_t)adm * ROWB + tid * 16, st->self[0][tid]);
+        store16(u.V + (size_t)adm * ROWB + tid * 16, st->self[1][tid]);
+      }
     }
   }
 }
@@ -588,15 +719,18 @@ struct StepShared {
   float s_l[GG::NG];
   Stash<GG> st;
   unsigned long long s_key[GG::NT / 64];
-  int s_victim;
+  int s_slot[GG::NT / 64];
 };
 
 // One decode step of one unit by the whole workgroup.  s_logit: LDS, at least
 // n_live + 1 floats.  score_lds / pos_lds: when not null, the unit's scores and
 // positions live in LDS (k entries each) instead of the state buffers.
-template <typename GG, int D>
+// With RES the cached rows are read from the LDS copy `res` (kept current by
+// the admission) and the step's inputs come from `in`.
+template <typename GG, int D, bool RES = false>
 __device__ __forceinline__ void unit_step(const DecodeArgs& a, int unit, StepShared<GG, D>& sh, float* s_logit,
-                                          float* score_lds, int32_t* pos_lds) {
+                                          float* score_lds, int32_t* pos_lds, const ResRows<GG>* res = nullptr,
+                                          const StepIn<GG>* in = nullptr) {
   constexpr int EPL = GG::EPL, LPR = GG::LPR, NG = GG::NG, NT = GG::NT, PF = GG::PF;
   const int tid = threadIdx.x;
   const StepView v(a);
@@ -608,10 +742,11 @@ __device__ __forceinline__ void unit_step(const DecodeArgs& a, int unit, StepSha
   const int gl = (tid & 63) & (GG::G - 1);
   const bool act = gl < LPR;
 
-  if (tid == 0) sh.s_victim = v.fixed_victim();  // overwritten by the argmin owner when the cache is full
-
   float qf[EPL];
-  load_input<GG>(u.q, act ? gl : 0, qf);
+  if constexpr (RES)
+    unpack_input<GG>(in->q, qf);
+  else
+    load_input<GG>(u.q, act ? gl : 0, qf);
   if (!act) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qf[e] = 0.f;
@@ -620,11 +755,14 @@ __device__ __forceinline__ void unit_step(const DecodeArgs& a, int unit, StepSha
   int ps_pf[PF];
   prefetch_scores<GG>(v, u, sc_pf, ps_pf);
 
-  float m = -INFINITY, lsum = 0.f;
+  float m = kNoMax, lsum = 0.f;
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  stream_rows<GG>(v, u, 0, v.n_att, qf, a.scale_log2, s_logit, &sh.st, m, lsum, o);
+  if constexpr (RES)
+    stream_rows<GG, 2, true>(v, u, 0, v.n_att, qf, a.scale_log2, s_logit, &sh.st, m, lsum, o, res, in);
+  else
+    stream_rows<GG>(v, u, 0, v.n_att, qf, a.scale_log2, s_logit, &sh.st, m, lsum, o);
 
   const GroupMerge<NG> gm = merge_groups<GG, D>(m, lsum, o, sh.s_o, sh.s_m, sh.s_l);
   const float invL = 1.f / gm.L;
@@ -634,7 +772,8 @@ __device__ __forceinline__ void unit_step(const DecodeArgs& a, int unit, StepSha
     for (int g = 0; g < NG; ++g) acc = fmaf(sh.s_o[g][c], gm.wg[g], acc);
     a.out[(size_t)unit * D + c] = acc * invL;
   }
-  finish_step<GG>(v, u, gm.M, invL, s_logit, sc_pf, ps_pf, &sh.st, sh.s_key, &sh.s_victim, a.evicted, unit);
+  finish_step<GG, RES>(v, u, gm.M, invL, s_logit, sc_pf, ps_pf, &sh.st, sh.s_key, sh.s_slot, a.evicted, unit,
+                       res, in);
 }
 
 template <typename T, typename C, int D, int NW>
@@ -695,6 +834,121 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 4
   }
 }
 
+// n_steps consecutive steps with the unit's whole state in LDS: its K and V rows
+// (and E4M3 row scales), scores and positions are read once at launch; a step
+// streams the rows from LDS, and its admission writes the admitted rows both to
+// LDS and to the state buffers; scores and positions go back at the end.  Each
+// step's inputs (q and the new token's rows) are loaded during the step before.
+// A workgroup holds 2k rows of LDS (k = 256, d = 128 bf16: 128 KB), so this
+// runs when that fits the device's per-workgroup LDS and there are no more
+// units than compute units.  Same arithmetic as decode_kernel, step for step.
+template <typename T, typename C, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_resident_kernel(DecodeArgs a, int n_steps, int live0) {
+  using GG = Geo<T, C, D, NW>;
+  constexpr int ROWB = GG::ROWB, NT = GG::NT;
+  __shared__ StepShared<GG, D> sh;
+  extern __shared__ float dynr[];  // K rows, V rows, [K scales, V scales], logits [k + 1], scores [k], positions [k]
+  const int k = a.k;
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x;
+  // Unquantized caches keep one row more in K and V: row k holds the decoded
+  // token, written at the end of the step before (the E4M3 path takes the
+  // token's exact row from registers).
+  constexpr int XR = GG::kQuant ? 0 : 1;
+  lds_char* base = (lds_char*)dynr;
+  ResRows<GG> res;
+  res.K = base;
+  res.V = base + (k + XR) * ROWB;
+  res.ks = res.vs = nullptr;
+  int words = 2 * (k + XR) * ROWB / 4;  // floats before the logits
+  if constexpr (GG::kQuant) {
+    res.ks = (lds_f32*)(base + 2 * k * ROWB);
+    res.vs = res.ks + k;
+    words += 2 * k;
+  }
+  float* s_logit = dynr + words;
+  float* s_score = s_logit + k + 1;
+  int32_t* s_pos = reinterpret_cast<int32_t*>(s_score + k);
+
+  const size_t ubase = (size_t)unit * k;
+  {
+    // the unit's rows, four 16-byte loads of each tensor in flight per thread
+    const char* Kg = (const char*)a.k_slots + ubase * ROWB;
+    const char* Vg = (const char*)a.v_slots + ubase * ROWB;
+    const int n16 = k * ROWB / 16;
+    for (int i0 = tid; i0 < n16; i0 += 4 * NT) {
+      uint4 kb[4], vb[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int i = min(i0 + w * NT, n16 - 1);
+        kb[w] = load16(Kg + (size_t)i * 16);
+        vb[w] = load16(Vg + (size_t)i * 16);
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int i = i0 + w * NT;
+        if (i < n16) {
+          lds_store16(res.K + i * 16, kb[w]);
+          lds_store16(res.V + i * 16, vb[w]);
+        }
+      }
+    }
+  }
+  for (int i = tid; i < k; i += NT) {
+    s_score[i] = a.score[ubase + i];
+    s_pos[i] = a.pos[ubase + i];
+    if constexpr (GG::kQuant) {
+      res.ks[i] = a.k_scale[ubase + i];
+      res.vs[i] = a.v_scale[ubase + i];
+    }
+  }
+  const size_t in_step = (size_t)a.units * GG::IROWB;
+  const int gl = (tid & 63) & (GG::G - 1);
+  const int chunk = gl < GG::LPR ? gl : 0;
+  StepIn<GG> cur, nxt;
+  load_step_in<GG>(UnitPtrs<GG>(a, unit, k), chunk, cur);
+  if constexpr (XR) {
+    if (tid < GG::LPR) {
+      lds_store16(res.K + k * ROWB + tid * 16, cur.k[0]);
+      lds_store16(res.V + k * ROWB + tid * 16, cur.v[0]);
+    }
+  }
+  __syncthreads();
+  for (int st = 0; st < n_steps; ++st) {
+    DecodeArgs as = a;
+    as.t = a.t + st;
+    const int n_live = min(live0 + st, k);
+    as.n_ring = min(as.t, a.r);
+    as.n_heavy = n_live - as.n_ring;
+    as.q = (const char*)a.q + st * in_step;
+    as.k_new = (const char*)a.k_new + st * in_step;
+    as.v_new = (const char*)a.v_new + st * in_step;
+    as.out = a.out + (size_t)st * a.units * D;
+    as.evicted = a.evicted ? a.evicted + (size_t)st * a.units : nullptr;
+    if (st + 1 < n_steps) {
+      DecodeArgs an = as;
+      an.q = (const char*)as.q + in_step;
+      an.k_new = (const char*)as.k_new + in_step;
+      an.v_new = (const char*)as.v_new + in_step;
+      load_step_in<GG>(UnitPtrs<GG>(an, unit, k), chunk, nxt);
+    }
+    unit_step<GG, D, true>(as, unit, sh, s_logit, s_score, s_pos, &res, &cur);
+    if constexpr (XR) {
+      // the next token's row; every read of row k in this step is behind the merge barrier
+      if (st + 1 < n_steps && tid < GG::LPR) {
+        lds_store16(res.K + k * ROWB + tid * 16, nxt.k[0]);
+        lds_store16(res.V + k * ROWB + tid * 16, nxt.v[0]);
+      }
+    }
+    __syncthreads();
+    cur = nxt;
+  }
+  for (int i = tid; i < k; i += NT) {
+    a.score[ubase + i] = s_score[i];
+    a.pos[ubase + i] = s_pos[i];
+  }
+}
+
 // Device-scope (agent) relaxed store and load: global_store / global_load with
 // sc1 on gfx950, coherent across the XCDs without a cache writeback.
 __device__ __forceinline__ void publish(float* p, float x) {
@@ -715,7 +969,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   __shared__ float s_l[NG];
   __shared__ Stash<GG> st;
   __shared__ unsigned long long s_key[NW];
-  __shared__ int s_victim;
+  __shared__ int s_slot[NW];
   __shared__ int s_last;
   extern __shared__ float s_logit[];  // [n_live + 1]
 
@@ -727,8 +981,6 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   const UnitPtrs<GG> u(a, unit, v.k);
   const int gl = (tid & 63) & (GG::G - 1);
   const bool act = gl < LPR;
-
-  if (tid == 0) s_victim = v.fixed_victim();
 
   float qf[EPL];
   load_input<GG>(u.q, act ? gl : 0, qf);
@@ -743,7 +995,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   const int per = (v.n_att + S - 1) / S;
   const int lo = min(v.n_att, part * per);
   const int hi = min(v.n_att, lo + per);
-  float m = -INFINITY, lsum = 0.f;
+  float m = kNoMax, lsum = 0.f;
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
@@ -868,12 +1120,29 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
     a.out[(size_t)unit * D + d] = acc * invL;
   }
   __syncthreads();
-  finish_step<GG>(v, u, M, invL, s_logit, sc_pf, ps_pf, &st, s_key, &s_victim, a.evicted, unit);
+  finish_step<GG>(v, u, M, invL, s_logit, sc_pf, ps_pf, &st, s_key, s_slot, a.evicted, unit);
   if (tid == 0) sp.counters[unit] = 0u;  // ready for the next step
 }
 
+// Dynamic LDS of the resident kernel: rows, E4M3 row scales, logits, scores, positions.
+template <typename T, typename C, int D>
+size_t resident_dyn_lds(int k) {
+  constexpr bool quant = std::is_same<C, e4m3>::value;
+  const size_t rows = quant ? (size_t)k : (size_t)k + 1;  // unquantized: one more row for the token
+  return 2 * rows * D * Elem<C>::kBytes + (quant ? (size_t)8 * k : 0) + (size_t)(3 * k + 1) * sizeof(float);
+}
+
 template <typename T, typename C, int D, int NW>
-hipError_t launch_multi_nw(const DecodeArgs& a, int n_steps, int live0, hipStream_t s) {
+hipError_t launch_multi_nw(const DecodeArgs& a, int n_steps, int live0, bool resident, hipStream_t s) {
+  if (resident) {
+    const size_t lds = resident_dyn_lds<T, C, D>(a.k);
+    const hipError_t e = hipFuncSetAttribute((const void*)decode_resident_kernel<T, C, D, NW>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_resident_kernel<T, C, D, NW>), dim3(a.units), dim3(NW * 64), lds, s, a, n_steps,
+                       live0);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)(3 * a.k + 1) * sizeof(float);
   hipLaunchKernelGGL((decode_multi_kernel<T, C, D, NW>), dim3(a.units), dim3(NW * 64), lds, s, a, n_steps,
                      live0);
@@ -912,23 +1181,34 @@ int multi_per_cu_t(int k, int head_dim, int waves) {
 }
 
 template <typename T, typename C, int D>
-hipError_t launch_multi_d(const DecodeArgs& a, int waves, int n_steps, int live0, hipStream_t s) {
+hipError_t launch_multi_d(const DecodeArgs& a, int waves, int n_steps, int live0, bool resident, hipStream_t s) {
   switch (waves) {
-    case 1: return launch_multi_nw<T, C, D, 1>(a, n_steps, live0, s);
-    case 2: return launch_multi_nw<T, C, D, 2>(a, n_steps, live0, s);
-    case 4: return launch_multi_nw<T, C, D, 4>(a, n_steps, live0, s);
-    case 8: return launch_multi_nw<T, C, D, 8>(a, n_steps, live0, s);
+    case 1: return launch_multi_nw<T, C, D, 1>(a, n_steps, live0, resident, s);
+    case 2: return launch_multi_nw<T, C, D, 2>(a, n_steps, live0, resident, s);
+    case 4: return launch_multi_nw<T, C, D, 4>(a, n_steps, live0, resident, s);
+    case 8: return launch_multi_nw<T, C, D, 8>(a, n_steps, live0, resident, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T, typename C>
-hipError_t launch_multi_t(const DecodeArgs& a, int head_dim, int waves, int n_steps, int live0, hipStream_t s) {
+hipError_t launch_multi_t(const DecodeArgs& a, int head_dim, int waves, int n_steps, int live0, bool resident,
+                          hipStream_t s) {
   switch (head_dim) {
-    case 64: return launch_multi_d<T, C, 64>(a, waves, n_steps, live0, s);
-    case 96: return launch_multi_d<T, C, 96>(a, waves, n_steps, live0, s);
-    case 128: return launch_multi_d<T, C, 128>(a, waves, n_steps, live0, s);
+    case 64: return launch_multi_d<T, C, 64>(a, waves, n_steps, live0, resident, s);
+    case 96: return launch_multi_d<T, C, 96>(a, waves, n_steps, live0, resident, s);
+    case 128: return launch_multi_d<T, C, 128>(a, waves, n_steps, live0, resident, s);
     default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, typename C>
+size_t resident_dyn_lds_t(int k, int head_dim) {
+  switch (head_dim) {
+    case 64: return resident_dyn_lds<T, C, 64>(k);
+    case 96: return resident_dyn_lds<T, C, 96>(k);
+    case 128: return resident_dyn_lds<T, C, 128>(k);
+    default: return (size_t)-1 / 2;
   }
 }
 
@@ -1023,6 +1303,17 @@ bool decode_multi_fits(int k, int dtype, int cache, int head_dim, int waves) {
   return decode_static_lds(dtype, cache, head_dim, waves) + (size_t)(3 * k + 1) * 4 <= kMaxLds;
 }
 
+size_t decode_resident_lds(int k, int dtype, int cache, int head_dim, int waves) {
+  size_t dyn;
+  if (cache == 1)
+    dyn = resident_dyn_lds_t<bf16, e4m3>(k, head_dim);
+  else if (dtype == 0)
+    dyn = resident_dyn_lds_t<float, float>(k, head_dim);
+  else
+    dyn = resident_dyn_lds_t<bf16, bf16>(k, head_dim);
+  return decode_static_lds(dtype, cache, head_dim, waves) + dyn;
+}
+
 int decode_multi_per_cu(int k, int dtype, int cache, int head_dim, int waves) {
   if (!decode_multi_fits(k, dtype, cache, head_dim, waves)) return 0;
   if (cache == 1) return dtype == 1 ? multi_per_cu_t<bf16, e4m3>(k, head_dim, waves) : 0;
@@ -1032,14 +1323,14 @@ int decode_multi_per_cu(int k, int dtype, int cache, int head_dim, int waves) {
 }
 
 hipError_t launch_decode_multi(const DecodeArgs& a, int dtype, int cache, int head_dim, int waves, int n_steps,
-                               int live0, hipStream_t s) {
+                               int live0, bool resident, hipStream_t s) {
   if (!decode_multi_fits(a.k, dtype, cache, head_dim, waves)) return hipErrorInvalidValue;
   if (cache == 1) {
     if (dtype != 1) return hipErrorInvalidValue;
-    return launch_multi_t<bf16, e4m3>(a, head_dim, waves, n_steps, live0, s);
+    return launch_multi_t<bf16, e4m3>(a, head_dim, waves, n_steps, live0, resident, s);
   }
-  if (dtype == 0) return launch_multi_t<float, float>(a, head_dim, waves, n_steps, live0, s);
-  if (dtype == 1) return launch_multi_t<bf16, bf16>(a, head_dim, waves, n_steps, live0, s);
+  if (dtype == 0) return launch_multi_t<float, float>(a, head_dim, waves, n_steps, live0, resident, s);
+  if (dtype == 1) return launch_multi_t<bf16, bf16>(a, head_dim, waves, n_steps, live0, resident, s);
   return hipErrorInvalidValue;
 }
 

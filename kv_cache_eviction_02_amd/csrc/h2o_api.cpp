@@ -22,7 +22,7 @@ bool valid_dims(const h2o_config* c) {
          (int64_t)c->recent + c->heavy >= 1 &&
          (c->policy == H2O_POLICY_H2O || c->policy == H2O_POLICY_STATIC || c->policy == H2O_POLICY_NAIVE) &&
          (c->steps_mode == H2O_STEPS_AUTO || c->steps_mode == H2O_STEPS_PER_STEP ||
-          c->steps_mode == H2O_STEPS_PERSISTENT) &&
+          c->steps_mode == H2O_STEPS_PERSISTENT || c->steps_mode == H2O_STEPS_RESIDENT) &&
          c->max_prompt >= 0 && c->max_prompt <= H2O_MAX_PROMPT &&
          (c->kv_dtype == H2O_F32 || c->kv_dtype == H2O_BF16) &&
          isfinite(c->scale) && c->scale >= 0.f && c->start_pos >= 0 && c->start_live >= 0 &&
@@ -96,6 +96,8 @@ h2o_status h2o_create(const h2o_config* cfg, const h2o_state* state, h2o_ctx** o
   c->scratch = nullptr;
   c->split_mem = nullptr;
   c->multi_capacity = -1;
+  c->cus = -1;
+  c->lds_limit = -1;
   c->split = h2o::SplitScratch{nullptr, nullptr, nullptr, 1};
   int cus = 256;  // compute units of the current device (MI355X: 256), asked only when
                   // the automatic choice could split
@@ -260,48 +262,82 @@ h2o_status h2o_decode_step(h2o_ctx* ctx, const void* q, const void* k_new, const
   return enqueue_step(ctx, q, k_new, v_new, out, evicted_pos, (hipStream_t)stream);
 }
 
+namespace {
+
+// Compute units and per-workgroup LDS of the ctx's device, asked once.
+void query_device(h2o_ctx* ctx) {
+  if (ctx->cus >= 0) return;
+  int dev = 0, cus = 0, lds = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) lds = 0;
+  ctx->cus = cus > 0 ? cus : 0;
+  ctx->lds_limit = lds > 0 ? lds : 0;
+}
+
+// The resident multi-step kernel applies: every unit's workgroup, holding all
+// of the unit's rows in LDS, gets a compute unit of its own.
+bool resident_fits(h2o_ctx* ctx) {
+  if (ctx->split.splits >= 2) return false;
+  query_device(ctx);
+  const int64_t units = (int64_t)ctx->cfg.batch * ctx->cfg.heads;
+  return units <= ctx->cus &&
+         (int64_t)h2o::decode_resident_lds(ctx->k, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype, ctx->cfg.head_dim,
+                                           ctx->waves) <= ctx->lds_limit &&
+         h2o::decode_multi_fits(ctx->k, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype, ctx->cfg.head_dim, ctx->waves);
+}
+
+// How h2o_decode_steps runs n_steps: H2O_STEPS_RESIDENT, H2O_STEPS_PERSISTENT
+// (one launch) or H2O_STEPS_PER_STEP.
+int steps_plan(h2o_ctx* ctx, int32_t n_steps) {
+  const int mode = ctx->cfg.steps_mode;
+  if (n_steps < 2 || ctx->split.splits >= 2 || mode == H2O_STEPS_PER_STEP) return H2O_STEPS_PER_STEP;
+  if ((mode == H2O_STEPS_AUTO || mode == H2O_STEPS_RESIDENT) && resident_fits(ctx)) return H2O_STEPS_RESIDENT;
+  if (mode == H2O_STEPS_RESIDENT) return H2O_STEPS_PER_STEP;
+  if (!h2o::decode_multi_fits(ctx->k, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype, ctx->cfg.head_dim, ctx->waves))
+    return H2O_STEPS_PER_STEP;
+  if (mode == H2O_STEPS_PERSISTENT) return H2O_STEPS_PERSISTENT;
+  // Automatic: one launch when every unit's workgroup is resident at once
+  // (else a unit waits for whole launches of the others), and either the
+  // decode has several wavefronts per unit or a step moves little data.
+  // Measured on MI355X: ahead of per-step launches at 2, 4 and 8 wavefronts
+  // per unit on every workload tried, behind with single-wave units of a
+  // bf16 cache (3584 units, k = 410: 127 against 117 us per step).
+  const size_t row_bytes = (size_t)ctx->cfg.head_dim *
+                           (ctx->cfg.cache_dtype == H2O_CACHE_E4M3 ? 1 : ctx->cfg.kv_dtype == H2O_BF16 ? 2 : 4);
+  const size_t n_units = (size_t)ctx->cfg.batch * ctx->cfg.heads;
+  const size_t step_bytes = n_units * ctx->k * 2 * row_bytes;  // cached K/V bytes one step streams
+  if (ctx->waves == 1 && step_bytes > ((size_t)64 << 20)) return H2O_STEPS_PER_STEP;
+  if (ctx->multi_capacity < 0) {
+    query_device(ctx);
+    const int per_cu = h2o::decode_multi_per_cu(ctx->k, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype,
+                                                ctx->cfg.head_dim, ctx->waves);
+    ctx->multi_capacity = per_cu > 0 ? (int64_t)per_cu * ctx->cus : 0;
+  }
+  return (int64_t)n_units <= ctx->multi_capacity ? H2O_STEPS_PERSISTENT : H2O_STEPS_PER_STEP;
+}
+
+}  // namespace
+
 h2o_status h2o_decode_steps(h2o_ctx* ctx, int32_t n_steps, const void* q, const void* k_new,
                             const void* v_new, float* out, int32_t* evicted_pos, void* stream) {
   if (!ctx || n_steps < 1 || !step_args_ok(q, k_new, v_new, out, evicted_pos)) return H2O_ERR_INVALID;
   if (!ctx->has_state) return H2O_ERR_STATE;
   if ((int64_t)ctx->t + n_steps >= INT32_MAX - 1) return H2O_ERR_STATE;
-  // cached K/V bytes one step streams, for the automatic choice
-  const size_t row_bytes = (size_t)ctx->cfg.head_dim *
-                           (ctx->cfg.cache_dtype == H2O_CACHE_E4M3 ? 1 : ctx->cfg.kv_dtype == H2O_BF16 ? 2 : 4);
-  const size_t step_bytes = (size_t)ctx->cfg.batch * ctx->cfg.heads * ctx->k * 2 * row_bytes;
-  const size_t n_units = (size_t)ctx->cfg.batch * ctx->cfg.heads;
-  bool persistent = ctx->cfg.steps_mode == H2O_STEPS_PERSISTENT;
-  if (ctx->cfg.steps_mode == H2O_STEPS_AUTO && n_steps > 1 && ctx->split.splits < 2 &&
-      (ctx->waves > 1 || step_bytes <= ((size_t)64 << 20))) {
-    // Automatic: one launch when every unit's workgroup is resident at once
-    // (else a unit waits for whole launches of the others), and either the
-    // decode has several wavefronts per unit or a step moves little data.
-    // Measured on MI355X: ahead of per-step launches at 2, 4 and 8 wavefronts
-    // per unit on every workload tried, behind with single-wave units of a
-    // bf16 cache (3584 units, k = 410: 127 against 117 us per step).
-    if (ctx->multi_capacity < 0) {
-      const int per_cu = h2o::decode_multi_per_cu(ctx->k, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype,
-                                                  ctx->cfg.head_dim, ctx->waves);
-      int dev = 0, cus = 0;
-      ctx->multi_capacity =
-          per_cu > 0 && hipGetDevice(&dev) == hipSuccess &&
-                  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0
-              ? (int64_t)per_cu * cus
-              : 0;
-    }
-    persistent = (int64_t)n_units <= ctx->multi_capacity;
-  }
-  if (n_steps > 1 && persistent && ctx->split.splits < 2 &&
-      h2o::decode_multi_fits(ctx->k, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype, ctx->cfg.head_dim, ctx->waves)) {
-    // one launch carries every unit through all n_steps
+  const int plan = steps_plan(ctx, n_steps);
+  if (plan != H2O_STEPS_PER_STEP) {
+    // one launch carries every unit through all n_steps (resident: with its rows in LDS)
     const h2o::DecodeArgs a = step_args(ctx, q, k_new, v_new, out, evicted_pos);
-    const hipError_t e = h2o::launch_decode_multi(a, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype, ctx->cfg.head_dim,
-                                                  ctx->waves, n_steps, ctx->n_live, (hipStream_t)stream);
+    const hipError_t e =
+        h2o::launch_decode_multi(a, ctx->cfg.kv_dtype, ctx->cfg.cache_dtype, ctx->cfg.head_dim, ctx->waves,
+                                 n_steps, ctx->n_live, plan == H2O_STEPS_RESIDENT, (hipStream_t)stream);
     if (e != hipSuccess) return from_hip(e);
     ctx->t += n_steps;
     ctx->n_live = (int64_t)ctx->n_live + n_steps < ctx->k ? ctx->n_live + n_steps : ctx->k;
     return H2O_OK;
   }
+  const size_t n_units = (size_t)ctx->cfg.batch * ctx->cfg.heads;
   const size_t in_step = n_units * ctx->cfg.head_dim * (ctx->cfg.kv_dtype == H2O_BF16 ? 2 : 4);
   const size_t out_step = n_units * ctx->cfg.head_dim;
   for (int32_t s = 0; s < n_steps; ++s) {
@@ -311,6 +347,12 @@ h2o_status h2o_decode_steps(h2o_ctx* ctx, int32_t n_steps, const void* q, const 
         evicted_pos ? evicted_pos + s * n_units : nullptr, (hipStream_t)stream);
     if (st != H2O_OK) return st;
   }
+  return H2O_OK;
+}
+
+h2o_status h2o_steps_launch(h2o_ctx* ctx, int32_t n_steps, int32_t* mode) {
+  if (!ctx || n_steps < 1 || !mode) return H2O_ERR_INVALID;
+  *mode = steps_plan(ctx, n_steps);
   return H2O_OK;
 }
 

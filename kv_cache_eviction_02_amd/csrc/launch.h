@@ -67,9 +67,12 @@ hipError_t launch_prefill(const PrefillArgs& a, int dtype, int cache, int head_d
 // n_steps consecutive steps in one launch (one workgroup per unit, no split):
 // `a` describes the first step, live0 = live slots before it; inputs and
 // outputs of step s start s * units rows further.  Requires
-// decode_multi_fits(a.k, ...).
+// decode_multi_fits(a.k, ...); with `resident` the unit's rows stay in LDS
+// (decode_resident_lds bytes per workgroup, one workgroup per compute unit).
 hipError_t launch_decode_multi(const DecodeArgs& a, int dtype, int cache, int head_dim, int waves, int n_steps,
-                               int live0, hipStream_t s);
+                               int live0, bool resident, hipStream_t s);
+// Static plus dynamic LDS of the resident multi-step kernel.
+size_t decode_resident_lds(int k, int dtype, int cache, int head_dim, int waves);
 
 // LDS a workgroup may take without opting in to more.
 constexpr size_t kMaxLds = 64 * 1024;

@@ -39,7 +39,8 @@ def test_library_exports_every_header_function():
     names = header_functions()
     assert names == sorted(["h2o_create", "h2o_prefill", "h2o_prefill_with_output", "h2o_prefill_no_alloc",
                             "h2o_decode_step", "h2o_decode_steps",
-                            "h2o_query", "h2o_launch_shape", "h2o_destroy", "h2o_status_string"])
+                            "h2o_query", "h2o_launch_shape", "h2o_steps_launch", "h2o_destroy",
+                            "h2o_status_string"])
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
@@ -90,7 +91,7 @@ def test_status_strings():
     (dict(recent=0, heavy=0), B.H2O_ERR_INVALID),                   # empty budget
     (dict(policy=3), B.H2O_ERR_INVALID),
     (dict(policy=-1), B.H2O_ERR_INVALID),
-    (dict(steps_mode=3), B.H2O_ERR_INVALID),
+    (dict(steps_mode=4), B.H2O_ERR_INVALID),
     (dict(heavy=-1), B.H2O_ERR_INVALID),
     (dict(max_prompt=-5), B.H2O_ERR_INVALID),
     (dict(max_prompt=(1 << 28) + 1), B.H2O_ERR_INVALID),
@@ -181,6 +182,22 @@ def test_no_alloc_prefill_checks_without_device_work():
     assert k2.h2o_prefill_no_alloc(None, FAKE, FAKE, FAKE, 16, None, None) == B.H2O_ERR_INVALID
 
 
+def test_steps_launch_without_device_work():
+    # one step, or a config that asks for per-step launches, plans per-step
+    # launches before any device query
+    for mode in (B.H2O_STEPS_AUTO, B.H2O_STEPS_PERSISTENT, B.H2O_STEPS_RESIDENT, B.H2O_STEPS_PER_STEP):
+        st, ctx = k2.h2o_create(cfg(steps_mode=mode), state())
+        assert st == B.H2O_OK
+        try:
+            assert k2.h2o_steps_launch(ctx, 1) == (B.H2O_OK, B.H2O_STEPS_PER_STEP)
+            if mode == B.H2O_STEPS_PER_STEP:
+                assert k2.h2o_steps_launch(ctx, 64) == (B.H2O_OK, B.H2O_STEPS_PER_STEP)
+            assert k2.h2o_steps_launch(ctx, 0)[0] == B.H2O_ERR_INVALID
+        finally:
+            k2.h2o_destroy(ctx)
+    assert B.load_library().h2o_steps_launch(None, 4, None) == B.H2O_ERR_INVALID
+
+
 def test_adopted_state_counters():
     st, ctx = k2.h2o_create(cfg(start_pos=100, start_live=8), state())
     assert st == B.H2O_OK
@@ -254,13 +271,13 @@ def test_lds_budget_of_large_e4m3_budget():
 def test_lds_limit_of_the_e4m3_decode_with_eight_wavefronts():
     # the single-step kernels keep k + 1 logits in LDS beside their static
     # arrays; for an E4M3 cache, d = 128 and 8 wavefronts the largest budget
-    # that fits is k = 7895 (the GPU tests run the split decode there)
+    # that fits is k = 7891 (the GPU tests run the split decode there)
     base = dict(head_dim=128, kv_dtype=B.H2O_BF16, cache_dtype=B.H2O_CACHE_E4M3, decode_waves=8,
                 decode_split=1)
-    st, ctx = k2.h2o_create(cfg(recent=3948, heavy=3947, **base), state(ks=FAKE, vs=FAKE))
+    st, ctx = k2.h2o_create(cfg(recent=3946, heavy=3945, **base), state(ks=FAKE, vs=FAKE))
     assert st == B.H2O_OK and ctx
     assert k2.h2o_destroy(ctx) == B.H2O_OK
-    st, ctx = k2.h2o_create(cfg(recent=3948, heavy=3948, **base), state(ks=FAKE, vs=FAKE))
+    st, ctx = k2.h2o_create(cfg(recent=3946, heavy=3946, **base), state(ks=FAKE, vs=FAKE))
     assert st == B.H2O_ERR_UNSUPPORTED and ctx is None
 
 

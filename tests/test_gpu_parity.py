@@ -285,11 +285,11 @@ def test_calls_are_ordered_on_the_callers_stream():
 # ---- the split decode at the LDS limit ------------------------------------------------------
 
 def test_split_decode_at_the_lds_limit():
-    """E4M3 cache with 8 wavefronts per workgroup at k = 7895, the largest
+    """E4M3 cache with 8 wavefronts per workgroup at k = 7891, the largest
     budget the create-time LDS check accepts there: the split kernel must take
     no more LDS than the fused one, so its launches run and match the oracle."""
-    wl = Workload(112, "lds_limit_e4m3", 1, 2, 128, 7950, 4, 3948, 3947, "bf16", "zipf", zipf_alpha=1.1)
-    assert wl.k == 7895
+    wl = Workload(112, "lds_limit_e4m3", 1, 2, 128, 7950, 4, 3946, 3945, "bf16", "zipf", zipf_alpha=1.1)
+    assert wl.k == 7891
     run_workload(wl, wl.units, wl.steps, decode_waves=8, decode_split=2, cache="e4m3", kv_every=2)
 
 
@@ -561,9 +561,10 @@ def test_run_twice_bitwise_identical():
 
 
 def _steps_vs_single(wl, n, split_at, cache_kind="input", policy="h2o", decode_waves=0, decode_split=1,
-                     steps_mode="persistent"):
+                     steps_mode="persistent", expect=None):
     """Run n steps as single h2o_decode_step calls and as h2o_decode_steps calls
-    (split at split_at); return both runs' outputs, evictions and final state."""
+    (split at split_at); return both runs' outputs, evictions and final state.
+    expect: the launch h2o_decode_steps must choose for the second call."""
     from kv_cache_eviction_02_amd import H2OCache
     prompt = stage_prompt(wl, "cuda")
     dq, dk, dv = stage_decode(wl, 0, n, "cuda")
@@ -575,6 +576,8 @@ def _steps_vs_single(wl, n, split_at, cache_kind="input", policy="h2o", decode_w
                          steps_mode=steps_mode if multi else "per_step")
         cache.prefill(*prompt)
         if multi:
+            if expect is not None:
+                assert cache.steps_launch(n - split_at) == expect
             parts = [(0, split_at), (split_at, n)]
             outs, evs = [], []
             for lo, hi in parts:
@@ -623,6 +626,39 @@ def test_decode_steps_equals_single_steps(name, n, split_at, cache_kind, policy,
         assert torch.equal(x, y)
 
 
+RESIDENT_CASES = [  # (workload, n, split point, cache, policy, waves)
+    ("llama7b_stream", 96, 40, "input", "h2o", 0),
+    ("llama7b_stream", 64, 17, "e4m3", "h2o", 0),
+    ("opt6.7b", 64, 30, "input", "h2o", 0),
+    ("opt6.7b", 48, 1, "e4m3", "naive", 0),
+    ("tiny_fp32", 64, 30, "input", "static", 1),
+    ("tiny_fp32", 64, 20, "input", "h2o", 4),
+    ("tiny_fp32", 40, 3, "input", "naive", 8),
+]
+
+
+@pytest.mark.parametrize("name,n,split_at,cache_kind,policy,waves", RESIDENT_CASES)
+def test_decode_steps_resident_equals_single_steps(name, n, split_at, cache_kind, policy, waves):
+    """h2o_decode_steps with every unit's K/V rows held in LDS across the
+    steps gives bit-identical outputs, evictions and state to single steps."""
+    say(f"[parity] resident decode_steps vs decode_step: {name}, {n} steps, {cache_kind}, {policy}, waves {waves}")
+    a, b = _steps_vs_single(WORKLOADS[name], n, split_at, cache_kind, policy, waves, steps_mode="resident",
+                            expect="resident")
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_long_stream_automatic_mode_is_resident():
+    """The long stream (32 units, k = 256, d = 128) fits in LDS: the automatic
+    multi-step mode keeps its rows there."""
+    from kv_cache_eviction_02_amd import H2OCache
+    wl = WORKLOADS["llama7b_stream"]
+    c = H2OCache(wl.batch, wl.heads, wl.head_dim, wl.recent, wl.heavy, wl.prompt, torch.bfloat16, wl.scale)
+    c.prefill(*stage_prompt(wl, "cuda"))
+    assert c.steps_launch(64) == "resident" and c.steps_launch(1) == "per_step"
+    c.close()
+
+
 @pytest.mark.parametrize("cache_kind", ["input", "e4m3"])
 @pytest.mark.parametrize("name", ["neox20b", "opt30b"])
 def test_decode_steps_automatic_mode_equals_single_steps(name, cache_kind):
@@ -639,12 +675,14 @@ def test_decode_steps_automatic_mode_equals_single_steps(name, cache_kind):
                                                               "ragged_f32_d96", "mid_prompt_f32_d128")],
                          ids=lambda w: w.name)
 @pytest.mark.parametrize("policy", ["h2o", "static", "naive"])
-def test_decode_steps_fill_phase_and_heavy_only(wl, policy):
+@pytest.mark.parametrize("steps_mode", ["persistent", "resident"])
+def test_decode_steps_fill_phase_and_heavy_only(wl, policy, steps_mode):
     """Multi-step calls through the filling phase (n_live grows inside the
     launch), and with recent = 0."""
-    say(f"[parity] decode_steps fill phase: {wl.name} {policy}")
+    say(f"[parity] decode_steps fill phase: {wl.name} {policy} {steps_mode}")
     for w in (wl, heavy_only(wl, wl.cid + 300)):
-        a, b = _steps_vs_single(w, w.steps, w.steps // 3, "input", policy, 0)
+        a, b = _steps_vs_single(w, w.steps, w.steps // 3, "input", policy, 0, steps_mode=steps_mode,
+                                expect=steps_mode)
         for x, y in zip(a, b):
             assert torch.equal(x, y)
 
