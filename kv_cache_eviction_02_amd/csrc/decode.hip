@@ -181,6 +181,10 @@ struct Stash {
   uint4 ring[2][GG::LPR];  // K, V of the ring slot leaving the window
   uint4 self[2][GG::LPR];  // K, V of the decoded token (cache format; not used for E4M3)
   float ring_scale[2];     // E4M3 row scales of the ring row
+  // E4M3: the decoded token's exact input rows, kept from the stream's first
+  // read of them for the quantized admission (a re-read at the end of a long
+  // stream would come from memory)
+  uint4 tok[2][GG::kQuant ? GG::IROWB / 16 : 1];
 };
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -350,10 +354,18 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
     // The decoded token (exact bf16 row) seeds row group 0 when it is in range.
     if (v.n_live >= lo && v.n_live < hi) {
       float kx[EPL];
-      if constexpr (RES)
+      if constexpr (RES) {
         unpack_input<GG>(in->k, kx);
-      else
-        load_input<GG>(u.kn, chunk, kx);
+      } else {
+        uint4 raw[GG::ICH];
+#pragma unroll
+        for (int i = 0; i < GG::ICH; ++i) raw[i] = load16(u.kn + (chunk * GG::ICH + i) * 16);
+        unpack_input<GG>(raw, kx);
+        if (grp == 0 && act) {
+#pragma unroll
+          for (int i = 0; i < GG::ICH; ++i) st->tok[0][chunk * GG::ICH + i] = raw[i];
+        }
+      }
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) d = fmaf(qf[e], kx[e], d);
@@ -362,10 +374,18 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
       if (grp == 0) {
         if (gl == 0) s_logit[v.n_live] = ls;
         float vx[EPL];
-        if constexpr (RES)
+        if constexpr (RES) {
           unpack_input<GG>(in->v, vx);
-        else
-          load_input<GG>(u.vn, chunk, vx);
+        } else {
+          uint4 raw[GG::ICH];
+#pragma unroll
+          for (int i = 0; i < GG::ICH; ++i) raw[i] = load16(u.vn + (chunk * GG::ICH + i) * 16);
+          unpack_input<GG>(raw, vx);
+          if (act) {
+#pragma unroll
+            for (int i = 0; i < GG::ICH; ++i) st->tok[1][chunk * GG::ICH + i] = raw[i];
+          }
+        }
         m = ls;
         lsum = 1.f;
 #pragma unroll
@@ -478,9 +498,12 @@ __device__ __forceinline__ GroupMerge<GG::NG> merge_groups(float m, float lsum, 
 
 // Quantize the decoded token's K and V rows into slot `slot` (E4M3 cache):
 // lanes [0, G) of wave 0 take K, lanes [G, 2G) take V, each lane 16 values.
-// With RES the codes and scales also go to the LDS copy of the rows.
-template <typename GG, bool RES = false>
-__device__ inline void admit_quantized(const UnitPtrs<GG>& u, int slot, const ResRows<GG>* res = nullptr) {
+// The exact rows come from the stash (TOK == 1), from the lane's own step
+// inputs (TOK == 2: lane tid holds chunk tid % G of both rows) or from memory
+// (TOK == 0).  With RES the codes and scales also go to the LDS copy of the rows.
+template <typename GG, bool RES = false, int TOK = 0>
+__device__ inline void admit_quantized(const UnitPtrs<GG>& u, int slot, const ResRows<GG>* res = nullptr,
+                                       const Stash<GG>* st = nullptr, const StepIn<GG>* in = nullptr) {
   constexpr int G = GG::G, LPR = GG::LPR, EPL = GG::EPL;
   const int tid = threadIdx.x;
   if (tid >= 2 * G) return;
@@ -488,7 +511,16 @@ __device__ inline void admit_quantized(const UnitPtrs<GG>& u, int slot, const Re
   const int c = tid & (G - 1);
   const bool act = c < LPR;
   float x[EPL];
-  load_input<GG>(is_v ? u.vn : u.kn, act ? c : 0, x);
+  if constexpr (TOK == 1) {
+    uint4 raw[GG::ICH];
+#pragma unroll
+    for (int i = 0; i < GG::ICH; ++i) raw[i] = st->tok[is_v ? 1 : 0][(act ? c : 0) * GG::ICH + i];
+    unpack_input<GG>(raw, x);
+  } else if constexpr (TOK == 2) {
+    unpack_input<GG>(is_v ? in->v : in->k, x);
+  } else {
+    load_input<GG>(is_v ? u.vn : u.kn, act ? c : 0, x);
+  }
   float amax = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
@@ -508,7 +540,12 @@ __device__ inline void admit_quantized(const UnitPtrs<GG>& u, int slot, const Re
 // softmax max M and 1/L.  Logits of rows [0, n_att) are in s_logit; the
 // scores this thread owns were prefetched into sc_pf / ps_pf; the ring row and
 // (unquantized caches) the new token's row are in the LDS stash.
-template <typename GG, bool RES = false>
+// TOK_STASHED: the stream of this workgroup read the decoded token's rows
+// (E4M3: they are in the stash); the split kernel's combining workgroup may not
+// have, and reads them from memory.
+// SL: the scores and positions are in LDS (u.score / u.pos point there) and
+// are read where they are used instead of being prefetched.
+template <typename GG, bool RES = false, bool TOK_STASHED = true, bool SL = false>
 __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG>& u, float M,
                                             float invL, float* s_logit, const float* sc_pf,
                                             const int* ps_pf, const Stash<GG>* st,
@@ -555,7 +592,14 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
     const int j = tid + i * NT;
-    if (j < v.n_live) ns_pf[i] = update(j, ns_pf[i], sc_pf[i], ps_pf[i]);
+    if (j < v.n_live) {
+      if constexpr (SL) {
+        const int s = v.slot_of(j);
+        ns_pf[i] = update(j, ns_pf[i], u.score[s], v.is_cand(s) ? u.pos[s] : 0);
+      } else {
+        ns_pf[i] = update(j, ns_pf[i], sc_pf[i], ps_pf[i]);
+      }
+    }
   }
   // Slots past the prefetched ones (budgets above PF * NT): their scores and
   // positions are loaded kRest at a time before any is used, one memory round
@@ -670,7 +714,7 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
     }
     if (adm >= 0) {
       if constexpr (GG::kQuant) {
-        admit_quantized<GG, RES>(u, adm, res);
+        admit_quantized<GG, RES, 2>(u, adm, res, st, in);
       } else if (tid < LPR) {
         store16(u.K + (size_t)adm * ROWB + tid * 16, in->k[0]);
         store16(u.V + (size_t)adm * ROWB + tid * 16, in->v[0]);
@@ -685,7 +729,7 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
     }
     if (adm >= 0) {
       if constexpr (GG::kQuant) {
-        admit_quantized<GG>(u, adm);
+        admit_quantized<GG, false, TOK_STASHED ? 1 : 0>(u, adm, nullptr, st);
       } else if (tid < LPR) {
         store16(u.K + (size_t)adm * ROWB + tid * 16, st->self[0][tid]);
         store16(u.V + (size_t)adm * ROWB + tid * 16, st->self[1][tid]);
@@ -727,7 +771,7 @@ struct StepShared {
 // positions live in LDS (k entries each) instead of the state buffers.
 // With RES the cached rows are read from the LDS copy `res` (kept current by
 // the admission) and the step's inputs come from `in`.
-template <typename GG, int D, bool RES = false>
+template <typename GG, int D, bool RES = false, bool SL = false>
 __device__ __forceinline__ void unit_step(const DecodeArgs& a, int unit, StepShared<GG, D>& sh, float* s_logit,
                                           float* score_lds, int32_t* pos_lds, const ResRows<GG>* res = nullptr,
                                           const StepIn<GG>* in = nullptr) {
@@ -751,9 +795,9 @@ __device__ __forceinline__ void unit_step(const DecodeArgs& a, int unit, StepSha
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qf[e] = 0.f;
   }
-  float sc_pf[PF];
-  int ps_pf[PF];
-  prefetch_scores<GG>(v, u, sc_pf, ps_pf);
+  float sc_pf[SL ? 1 : PF];
+  int ps_pf[SL ? 1 : PF];
+  if constexpr (!SL) prefetch_scores<GG>(v, u, sc_pf, ps_pf);
 
   float m = kNoMax, lsum = 0.f;
   float o[EPL];
@@ -772,8 +816,8 @@ __device__ __forceinline__ void unit_step(const DecodeArgs& a, int unit, StepSha
     for (int g = 0; g < NG; ++g) acc = fmaf(sh.s_o[g][c], gm.wg[g], acc);
     a.out[(size_t)unit * D + c] = acc * invL;
   }
-  finish_step<GG, RES>(v, u, gm.M, invL, s_logit, sc_pf, ps_pf, &sh.st, sh.s_key, sh.s_slot, a.evicted, unit,
-                       res, in);
+  finish_step<GG, RES, true, SL>(v, u, gm.M, invL, s_logit, sc_pf, ps_pf, &sh.st, sh.s_key, sh.s_slot, a.evicted,
+                                 unit, res, in);
 }
 
 template <typename T, typename C, int D, int NW>
@@ -825,7 +869,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 4
     as.v_new = (const char*)a.v_new + st * in_step;
     as.out = a.out + (size_t)st * a.units * D;
     as.evicted = a.evicted ? a.evicted + (size_t)st * a.units : nullptr;
-    unit_step<GG, D>(as, unit, sh, s_logit, s_score, s_pos);
+    unit_step<GG, D, false, true>(as, unit, sh, s_logit, s_score, s_pos);
     __syncthreads();
   }
   for (int i = threadIdx.x; i < k; i += GG::NT) {
@@ -932,7 +976,7 @@ __global__ __launch_bounds__(NW * 64) void decode_resident_kernel(DecodeArgs a, 
       an.v_new = (const char*)as.v_new + in_step;
       load_step_in<GG>(UnitPtrs<GG>(an, unit, k), chunk, nxt);
     }
-    unit_step<GG, D, true>(as, unit, sh, s_logit, s_score, s_pos, &res, &cur);
+    unit_step<GG, D, true, true>(as, unit, sh, s_logit, s_score, s_pos, &res, &cur);
     if constexpr (XR) {
       // the next token's row; every read of row k in this step is behind the merge barrier
       if (st + 1 < n_steps && tid < GG::LPR) {
@@ -988,10 +1032,6 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qf[e] = 0.f;
   }
-  float sc_pf[PF];
-  int ps_pf[PF];
-  prefetch_scores<GG>(v, u, sc_pf, ps_pf);
-
   const int per = (v.n_att + S - 1) / S;
   const int lo = min(v.n_att, part * per);
   const int hi = min(v.n_att, lo + per);
@@ -1046,6 +1086,11 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   float* s_pl = s_pm + 64;
   constexpr int kBatch = 8;
   const float* up = sp.partials + (size_t)unit * S * (D + 2);
+  // Only this workgroup updates the scores: their loads start here, in flight
+  // with the partials'.
+  float sc_pf[PF];
+  int ps_pf[PF];
+  prefetch_scores<GG>(v, u, sc_pf, ps_pf);
   // The rows the admission writes (still intact: only this workgroup writes
   // the unit's state) and the partials' maxima and sums go into registers
   // first, in flight with the logits, and into LDS after them.
@@ -1120,7 +1165,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
     a.out[(size_t)unit * D + d] = acc * invL;
   }
   __syncthreads();
-  finish_step<GG>(v, u, M, invL, s_logit, sc_pf, ps_pf, &st, s_key, s_slot, a.evicted, unit);
+  finish_step<GG, false, false>(v, u, M, invL, s_logit, sc_pf, ps_pf, &st, s_key, s_slot, a.evicted, unit);
   if (tid == 0) sp.counters[unit] = 0u;  // ready for the next step
 }
 

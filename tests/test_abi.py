@@ -270,15 +270,21 @@ def test_lds_budget_of_large_e4m3_budget():
 
 def test_lds_limit_of_the_e4m3_decode_with_eight_wavefronts():
     # the single-step kernels keep k + 1 logits in LDS beside their static
-    # arrays; for an E4M3 cache, d = 128 and 8 wavefronts the largest budget
-    # that fits is k = 7891 (the GPU tests run the split decode there)
+    # arrays: for an E4M3 cache, d = 128 and 8 wavefronts about 64 KB - 34 KB
+    # of static arrays leaves room for about 7800 budget slots (the GPU tests
+    # run the split decode at the largest accepted one)
+    from lds_limit import largest_budget
+    k = largest_budget(128, B.H2O_CACHE_E4M3, 8)
+    assert 7500 < k < 8000
     base = dict(head_dim=128, kv_dtype=B.H2O_BF16, cache_dtype=B.H2O_CACHE_E4M3, decode_waves=8,
                 decode_split=1)
-    st, ctx = k2.h2o_create(cfg(recent=3946, heavy=3945, **base), state(ks=FAKE, vs=FAKE))
+    st, ctx = k2.h2o_create(cfg(recent=(k + 1) // 2, heavy=k // 2, **base), state(ks=FAKE, vs=FAKE))
     assert st == B.H2O_OK and ctx
     assert k2.h2o_destroy(ctx) == B.H2O_OK
-    st, ctx = k2.h2o_create(cfg(recent=3946, heavy=3946, **base), state(ks=FAKE, vs=FAKE))
+    st, ctx = k2.h2o_create(cfg(recent=(k + 2) // 2, heavy=(k + 1) // 2, **base), state(ks=FAKE, vs=FAKE))
     assert st == B.H2O_ERR_UNSUPPORTED and ctx is None
+    # with four wavefronts the whole ABI range fits
+    assert largest_budget(128, B.H2O_CACHE_E4M3, 4) == B.H2O_MAX_K
 
 
 def test_launch_shape_reports_the_automatic_choices():

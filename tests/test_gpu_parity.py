@@ -285,11 +285,16 @@ def test_calls_are_ordered_on_the_callers_stream():
 # ---- the split decode at the LDS limit ------------------------------------------------------
 
 def test_split_decode_at_the_lds_limit():
-    """E4M3 cache with 8 wavefronts per workgroup at k = 7891, the largest
-    budget the create-time LDS check accepts there: the split kernel must take
+    """E4M3 cache with 8 wavefronts per workgroup at the largest budget the
+    create-time LDS check accepts there (about 7890): the split kernel must take
     no more LDS than the fused one, so its launches run and match the oracle."""
-    wl = Workload(112, "lds_limit_e4m3", 1, 2, 128, 7950, 4, 3946, 3945, "bf16", "zipf", zipf_alpha=1.1)
-    assert wl.k == 7891
+    from kv_cache_eviction_02_amd import binding as B
+    from lds_limit import largest_budget
+    k = largest_budget(128, B.H2O_CACHE_E4M3, 8)
+    assert 7500 < k < 8000
+    wl = Workload(112, "lds_limit_e4m3", 1, 2, 128, k + 60, 4, (k + 1) // 2, k // 2, "bf16", "zipf",
+                  zipf_alpha=1.1)
+    say(f"[parity] split decode at the LDS limit: k = {k}")
     run_workload(wl, wl.units, wl.steps, decode_waves=8, decode_split=2, cache="e4m3", kv_every=2)
 
 
