@@ -441,6 +441,9 @@ def main():
                     help="one h2o_decode_step call per step instead of one h2o_decode_steps call")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a device copy of this size (for counter scaling)")
+    ap.add_argument("--no-device-tools", action="store_true",
+                    help="skip the rocminfo / rocm-smi records (for runs under a profiler, whose "
+                         "preload has already opened the GPU)")
     ap.add_argument("--cpu-units-per-worker", type=int, default=32)
     ap.add_argument("--cpu-steps", type=int, default=128)
     args = ap.parse_args()
@@ -477,8 +480,8 @@ def main():
         sys.exit("an E4M3 cache takes bf16 inputs")
     # device listing and clocks from the ROCm tools, in child processes, before this
     # process touches the GPU
-    agent = rocminfo_record()
-    clocks = smi_clocks()
+    agent = {} if args.no_device_tools else rocminfo_record()
+    clocks = {} if args.no_device_tools else smi_clocks()
     g = run_gpu(wl, steps, warmup, args.decode_waves, args.copy_calibration_mib, args.single_step_calls,
                 args.decode_split, args.cache, args.policy, not args.no_streaming)
     ms_per_step = g["region_ms"] / steps

@@ -426,12 +426,26 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   }
 
   uint4 rk[RT::PER_T];
-  auto fetch = [&](int ch) __attribute__((always_inline)) {
+  // A chunk wholly below kend is read at a per-thread 32-bit offset from the
+  // chunk's (uniform) base; only the block's last chunk clamps its rows.
+  uint32_t thr_off[RT::PER_T];
 #pragma unroll
-    for (int u = 0; u < RT::PER_T; ++u) {
-      const int idx = min(tid + u * kWaves * 64, RT::PIECES - 1);
-      const int key = min(ch * RT::KC + idx / (RT::ROWB / 16), kend - 1);
-      rk[u] = load16(Kb + (size_t)key * RT::ROWB + (idx % (RT::ROWB / 16)) * 16);
+  for (int u = 0; u < RT::PER_T; ++u) {
+    const int idx = min(tid + u * kWaves * 64, RT::PIECES - 1);
+    thr_off[u] = (idx / (RT::ROWB / 16)) * RT::ROWB + (idx % (RT::ROWB / 16)) * 16;
+  }
+  auto fetch = [&](int ch) __attribute__((always_inline)) {
+    if ((ch + 1) * RT::KC <= kend) {  // uniform
+      const char* cb = Kb + (size_t)ch * RT::KC * RT::ROWB;
+#pragma unroll
+      for (int u = 0; u < RT::PER_T; ++u) rk[u] = load16(cb + thr_off[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < RT::PER_T; ++u) {
+        const int idx = min(tid + u * kWaves * 64, RT::PIECES - 1);
+        const int key = min(ch * RT::KC + idx / (RT::ROWB / 16), kend - 1);
+        rk[u] = load16(Kb + (size_t)key * RT::ROWB + (idx % (RT::ROWB / 16)) * 16);
+      }
     }
   };
   auto stash = [&](int b) __attribute__((always_inline)) {
@@ -439,7 +453,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
     for (int u = 0; u < RT::PER_T; ++u) {
       const int idx = tid + u * kWaves * 64;
-      if (idx < RT::PIECES)
+      if (RT::PIECES % (kWaves * 64) == 0 || idx < RT::PIECES)  // no branch when the block covers the chunk evenly
         *reinterpret_cast<uint4*>(kl + (idx / (RT::ROWB / 16)) * RT::KSTR + (idx % (RT::ROWB / 16)) * 16) = rk[u];
     }
   };
@@ -455,17 +469,26 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       for (int q = 0; q < QS; ++q) s[sub][q] = tile_dot<T, D>(fk, fq[q]);
     }
   };
+  // The only chunk that needs the causal mask is the wavefront's diagonal one
+  // (c0 = qw0): key 16*sub + 4g + i of it is kept for query qw0 + 16q + l%16 iff
+  // 16*sub + i <= 16q + l%16 - 4g.  Its 0 / -inf terms are set once.
+  float diag[QS][2][4];
+#pragma unroll
+  for (int q = 0; q < QS; ++q) {
+    const int t = q * kTile + (lane & 15) - 4 * g;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) diag[q][sub][i] = sub * kTile + i <= t ? 0.f : -INFINITY;
+  }
   auto soft = [&](auto mask_tag, int ch, f32x4 (&s)[2][QS]) __attribute__((always_inline)) {
     if constexpr (decltype(mask_tag)::value) {
-      // key 16*sub + 4g + i of the chunk is kept for query qi iff 16*sub + i <= qi - c0 - 4g
 #pragma unroll
-      for (int q = 0; q < QS; ++q) {
-        const int t = qw0 + q * kTile + (lane & 15) - ch * RT::KC - 4 * g;
+      for (int q = 0; q < QS; ++q)
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s[sub][q][i] = sub * kTile + i <= t ? s[sub][q][i] : -INFINITY;
-      }
+          for (int i = 0; i < 4; ++i) s[sub][q][i] += diag[q][sub][i];
     }
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
@@ -487,10 +510,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   auto active = [&](int ch) { return ch < nch && ch * RT::KC <= qw_last; };  // uniform
   // one pipeline stage: MFMAs of chunk ch + 1 into nxt, exponentials of chunk ch from cur
   auto stage = [&](int ch, f32x4 (&cur)[2][QS], f32x4 (&nxt)[2][QS]) __attribute__((always_inline)) {
+    const bool diag = ch * RT::KC + RT::KC - 1 > qw0;
     if (ch + 2 < nch) fetch(ch + 2);
     if (active(ch + 1)) mult(ch + 1, nxt);
     if (active(ch)) {
-      if (ch * RT::KC + RT::KC - 1 > qw0)
+      if (diag)
         soft(std::true_type{}, ch, cur);
       else
         soft(std::false_type{}, ch, cur);
@@ -593,21 +617,36 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   // Unconditional chunk loads (row clamped to P - 1); rows past P are masked.
   uint4 rq[CT::PER_T];
   float rl = 0.f;
-  auto fetch = [&](int ch) __attribute__((always_inline)) {
+  // A chunk wholly inside the prompt is read at a per-thread 32-bit offset from
+  // the chunk's (uniform) base; only the last chunk clamps its rows.
+  uint32_t thr_off[CT::PER_T];
 #pragma unroll
-    for (int u = 0; u < CT::PER_T; ++u) {
-      const int idx = min(tid + u * kWaves * 64, CT::PIECES - 1);
-      const int row = min(ch * CT::QC + idx / (CT::ROWB / 16), P - 1);
-      rq[u] = load16(Qb + (size_t)row * CT::ROWB + (idx % (CT::ROWB / 16)) * 16);
+  for (int u = 0; u < CT::PER_T; ++u) {
+    const int idx = min(tid + u * kWaves * 64, CT::PIECES - 1);
+    thr_off[u] = (idx / (CT::ROWB / 16)) * CT::ROWB + (idx % (CT::ROWB / 16)) * 16;
+  }
+  auto fetch = [&](int ch) __attribute__((always_inline)) {
+    if ((ch + 1) * CT::QC <= P) {  // uniform
+      const char* cb = Qb + (size_t)ch * CT::QC * CT::ROWB;
+#pragma unroll
+      for (int u = 0; u < CT::PER_T; ++u) rq[u] = load16(cb + thr_off[u]);
+      if (tid < CT::QC) rl = lse[ch * CT::QC + tid];
+    } else {
+#pragma unroll
+      for (int u = 0; u < CT::PER_T; ++u) {
+        const int idx = min(tid + u * kWaves * 64, CT::PIECES - 1);
+        const int row = min(ch * CT::QC + idx / (CT::ROWB / 16), P - 1);
+        rq[u] = load16(Qb + (size_t)row * CT::ROWB + (idx % (CT::ROWB / 16)) * 16);
+      }
+      if (tid < CT::QC) rl = lse[min(ch * CT::QC + tid, P - 1)];
     }
-    if (tid < CT::QC) rl = lse[min(ch * CT::QC + tid, P - 1)];
   };
   auto stash = [&](int b) __attribute__((always_inline)) {
     char* ql = smem + b * CT::BUF;
 #pragma unroll
     for (int u = 0; u < CT::PER_T; ++u) {
       const int idx = tid + u * kWaves * 64;
-      if (idx < CT::PIECES)
+      if (CT::PIECES % (kWaves * 64) == 0 || idx < CT::PIECES)  // no branch when the block covers the chunk evenly
         *reinterpret_cast<uint4*>(ql + (idx / (CT::ROWB / 16)) * CT::QSTR + (idx % (CT::ROWB / 16)) * 16) =
             rq[u];
     }
@@ -627,9 +666,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       for (int q = 0; q < QS; ++q) s[sub][q] = tile_dot<T, D>(fq, fk[q]);
     }
   };
+  // The wavefront's diagonal query chunk (c0 = j0) inside the prompt needs
+  // only the causal mask: query c0 + 16*sub + 4g + i counts for key
+  // j0 + 16q + l%16 iff i >= 16q + l%16 - 16*sub - 4g.  Its 0 / -inf terms are
+  // set once; the last chunk of a ragged prompt and the last-row-only mode
+  // take the general test.
+  float diag[2][QS][4];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int q = 0; q < QS; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        diag[sub][q][i] = i >= q * kTile + (lane & 15) - sub * kTile - g4 ? 0.f : -INFINITY;
   auto soft = [&](auto edge_tag, int ch, const f32x4 (&s)[2][QS], const float4 (&lq)[2])
                   __attribute__((always_inline)) {
-    constexpr bool edge = decltype(edge_tag)::value;
+    constexpr int edge = decltype(edge_tag)::value;  // 0 interior, 1 diagonal, 2 general
     const int c0 = ch * CT::QC;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -637,9 +689,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
       for (int q = 0; q < QS; ++q) {
         float e[4];
-        if constexpr (!edge) {
+        if constexpr (edge == 0) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) e[i] = fast_exp2(fmaf(s[sub][q][i], sc, -lv[i]));
+        } else if constexpr (edge == 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) e[i] = fast_exp2(fmaf(s[sub][q][i], sc, -lv[i]) + diag[sub][q][i]);
         } else {
           // query row base + i counts iff lo <= i < hi (causal, inside the prompt,
           // and the last row only for the naive policy); masked terms get the
@@ -659,14 +714,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   auto active = [&](int ch) { return ch < nch && w_last >= j0 && (ch + 1) * CT::QC - 1 >= j0; };
   auto stage = [&](int ch, f32x4 (&cur)[2][QS], float4 (&lcur)[2], f32x4 (&nxt)[2][QS], float4 (&lnxt)[2])
                    __attribute__((always_inline)) {
+    const int c0 = ch * CT::QC;
     if (ch + 2 < nch) fetch(ch + 2);
     if (active(ch + 1)) mult(ch + 1, nxt, lnxt);
     if (active(ch)) {
-      const int c0 = ch * CT::QC;
-      if (last_only || c0 < j0 + CT::ROWS - 1 || c0 + CT::QC > P)
-        soft(std::true_type{}, ch, cur, lcur);
+      if (last_only || c0 + CT::QC > P)
+        soft(std::integral_constant<int, 2>{}, ch, cur, lcur);
+      else if (c0 < j0 + CT::ROWS - 1)
+        soft(std::integral_constant<int, 1>{}, ch, cur, lcur);
       else
-        soft(std::false_type{}, ch, cur, lcur);
+        soft(std::integral_constant<int, 0>{}, ch, cur, lcur);
     }
     if (ch + 2 < nch) stash((ch - ch0) & 1);  // chunk ch + 2 replaces chunk ch, read one stage ago
     __syncthreads();
