@@ -21,8 +21,10 @@
 //              positions, then the gather of the kept K/V rows into slots
 //              (quantized to E4M3 with per-row scales for an E4M3 cache).
 // The moving operand of both sweeps goes through LDS in chunks of 32 rows
-// shared by a block's four wavefronts; loads of the next chunk are in flight
-// while the current one is multiplied.
+// shared by a block's four wavefronts, staged through registers one stage
+// ahead.  In each stage a wavefront reads the next chunk's fragments from LDS,
+// runs the current chunk's exponentials while they arrive, then the next
+// chunk's MFMAs.
 //
 // MFMA use: v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (f32).
 // Lane l supplies row l % 16 of a 16-row tile and the contiguous quarter
@@ -378,6 +380,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 #ifndef H2O_ROW_QS
 #define H2O_ROW_QS 2
 #endif
+// A kernel argument used inside a sweep's loop, read into its SGPR here.  The
+// argument arrives by a scalar load, and scalar loads share the lgkm counter
+// with LDS reads but complete out of order: were the load left to the loop's
+// first use, the wait for it there would be lgkmcnt(0) in every stage, holding
+// the exponentials until the next chunk's LDS reads had returned.
+__device__ inline float pin_arg(float v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
 template <typename T, int D>
 struct RowTile {
   static constexpr int QS = sizeof(T) == 2 ? H2O_ROW_QS : 2;  // fixed query subtiles per wavefront
@@ -413,7 +425,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const int nch = (kend + RT::KC - 1) / RT::KC;
   const char* Qb = (const char*)a.pq + (size_t)unit * P * RT::ROWB;
   const char* Kb = (const char*)a.pk + (size_t)unit * P * RT::ROWB;
-  const float sc = a.scale_log2;
+  const float sc = pin_arg(a.scale_log2);
 
   Frag<T, D> fq[QS];
 #pragma unroll
@@ -459,15 +471,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   };
   // Keys past kend hold copies of row kend - 1: they follow every query of the
   // block that is < P, so the causal mask removes them.
-  auto mult = [&](int ch, f32x4 (&s)[2][QS]) __attribute__((always_inline)) {
+  auto read = [&](int ch, Frag<T, D> (&fk)[2]) __attribute__((always_inline)) {
     const char* kl = smem + (ch & 1) * RT::BUF;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      Frag<T, D> fk;
-      load_lds_frag<T, D>(fk, kl, sub * kTile, RT::KSTR, lane);
+    for (int sub = 0; sub < 2; ++sub) load_lds_frag<T, D>(fk[sub], kl, sub * kTile, RT::KSTR, lane);
+  };
+  auto mult = [&](const Frag<T, D> (&fk)[2], f32x4 (&s)[2][QS]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int q = 0; q < QS; ++q) s[sub][q] = tile_dot<T, D>(fk, fq[q]);
-    }
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int q = 0; q < QS; ++q) s[sub][q] = tile_dot<T, D>(fk[sub], fq[q]);
   };
   // The only chunk that needs the causal mask is the wavefront's diagonal one
   // (c0 = qw0): key 16*sub + 4g + i of it is kept for query qw0 + 16q + l%16 iff
@@ -508,22 +521,28 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     }
   };
   auto active = [&](int ch) { return ch < nch && ch * RT::KC <= qw_last; };  // uniform
-  // one pipeline stage: MFMAs of chunk ch + 1 into nxt, exponentials of chunk ch from cur
-  auto stage = [&](int ch, f32x4 (&cur)[2][QS], f32x4 (&nxt)[2][QS]) __attribute__((always_inline)) {
+  // One pipeline stage: the LDS reads of chunk ch + 1 go out first, the
+  // exponentials of chunk ch (S tiles from the stage before) cover their
+  // latency, and the MFMAs of chunk ch + 1 then overwrite the same S registers;
+  // their results are not needed before the next stage.
+  auto stage = [&](int ch, f32x4 (&s)[2][QS]) __attribute__((always_inline)) {
     const bool diag = ch * RT::KC + RT::KC - 1 > qw0;
+    const bool next = active(ch + 1);
     if (ch + 2 < nch) fetch(ch + 2);
-    if (active(ch + 1)) mult(ch + 1, nxt);
+    Frag<T, D> fk[2];
+    if (next) read(ch + 1, fk);
     if (active(ch)) {
       if (diag)
-        soft(std::true_type{}, ch, cur);
+        soft(std::true_type{}, ch, s);
       else
-        soft(std::false_type{}, ch, cur);
+        soft(std::false_type{}, ch, s);
     }
+    if (next) mult(fk, s);
     if (ch + 2 < nch) stash(ch & 1);  // chunk ch + 2 replaces chunk ch, read one stage ago
     __syncthreads();
   };
 
-  f32x4 sa[2][QS], sb[2][QS];
+  f32x4 s[2][QS];
   fetch(0);
   stash(0);
   if (nch > 1) {
@@ -531,12 +550,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     stash(1);
   }
   __syncthreads();
-  if (active(0)) mult(0, sa);
-  __syncthreads();  // every wavefront has read chunk 0 before chunk 2 replaces it
-  for (int ch = 0; ch < nch; ch += 2) {
-    stage(ch, sa, sb);
-    if (ch + 1 < nch) stage(ch + 1, sb, sa);
+  if (active(0)) {
+    Frag<T, D> fk[2];
+    read(0, fk);
+    mult(fk, s);
   }
+  __syncthreads();  // every wavefront has read chunk 0 before chunk 2 replaces it
+  for (int ch = 0; ch < nch; ++ch) stage(ch, s);
 
   if (qw0 >= P) return;
 #pragma unroll
@@ -600,7 +620,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const char* Qb = (const char*)a.pq + (size_t)unit * P * CT::ROWB;
   const char* Kb = (const char*)a.pk + (size_t)unit * P * CT::ROWB;
   const float* lse = a.row_lse + (size_t)unit * stride;
-  const float sc = a.scale_log2;
+  const float sc = pin_arg(a.scale_log2);
   const bool last_only = a.last_row_only != 0;
   const int q_lo = last_only ? P - 1 : 0;              // first query row that counts
   const int ch0 = (last_only ? P - 1 : jb0) / CT::QC;  // first chunk the block needs
@@ -641,6 +661,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       if (tid < CT::QC) rl = lse[min(ch * CT::QC + tid, P - 1)];
     }
   };
+  // Chunk c's rows and lse values go to buffer (c - ch0) & 1.
   auto stash = [&](int b) __attribute__((always_inline)) {
     char* ql = smem + b * CT::BUF;
 #pragma unroll
@@ -652,33 +673,29 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     }
     if (tid < CT::QC) reinterpret_cast<float*>(ql + CT::QC * CT::QSTR)[tid] = rl;
   };
-  // S tiles of a chunk (acc[i]: query 4g + i of the subtile, key lane % 16) and the
-  // chunk's lse, both into registers: the buffer is refilled one stage later.
-  auto mult = [&](int ch, f32x4 (&s)[2][QS], float4 (&lq)[2]) __attribute__((always_inline)) {
+  // A chunk's query fragments and lse values, into registers (the buffer is
+  // refilled one stage later), then its S tiles (acc[i]: query 4g + i of the
+  // subtile, key lane % 16).
+  auto read = [&](int ch, Frag<T, D> (&fq)[2]) __attribute__((always_inline)) {
     const char* ql = smem + ((ch - ch0) & 1) * CT::BUF;
-    const float* ll = reinterpret_cast<const float*>(ql + CT::QC * CT::QSTR);
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      Frag<T, D> fq;
-      load_lds_frag<T, D>(fq, ql, sub * kTile, CT::QSTR, lane);
-      lq[sub] = *reinterpret_cast<const float4*>(ll + sub * kTile + g4);
+    for (int sub = 0; sub < 2; ++sub) load_lds_frag<T, D>(fq[sub], ql, sub * kTile, CT::QSTR, lane);
+  };
+  auto read_lse = [&](int ch, float4 (&lq)[2]) __attribute__((always_inline)) {
+    const float* ll = reinterpret_cast<const float*>(smem + ((ch - ch0) & 1) * CT::BUF + CT::QC * CT::QSTR);
 #pragma unroll
-      for (int q = 0; q < QS; ++q) s[sub][q] = tile_dot<T, D>(fq, fk[q]);
-    }
+    for (int sub = 0; sub < 2; ++sub) lq[sub] = *reinterpret_cast<const float4*>(ll + sub * kTile + g4);
+  };
+  auto mult = [&](const Frag<T, D> (&fq)[2], f32x4 (&s)[2][QS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int q = 0; q < QS; ++q) s[sub][q] = tile_dot<T, D>(fq[sub], fk[q]);
   };
   // The wavefront's diagonal query chunk (c0 = j0) inside the prompt needs
   // only the causal mask: query c0 + 16*sub + 4g + i counts for key
-  // j0 + 16q + l%16 iff i >= 16q + l%16 - 16*sub - 4g.  Its 0 / -inf terms are
-  // set once; the last chunk of a ragged prompt and the last-row-only mode
-  // take the general test.
-  float diag[2][QS][4];
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-    for (int q = 0; q < QS; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        diag[sub][q][i] = i >= q * kTile + (lane & 15) - sub * kTile - g4 ? 0.f : -INFINITY;
+  // j0 + 16q + l%16 iff i >= 16q + l%16 - 16*sub - 4g.  The last chunk of a
+  // ragged prompt and the last-row-only mode take the general test.
   auto soft = [&](auto edge_tag, int ch, const f32x4 (&s)[2][QS], const float4 (&lq)[2])
                   __attribute__((always_inline)) {
     constexpr int edge = decltype(edge_tag)::value;  // 0 interior, 1 diagonal, 2 general
@@ -694,7 +711,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
           for (int i = 0; i < 4; ++i) e[i] = fast_exp2(fmaf(s[sub][q][i], sc, -lv[i]));
         } else if constexpr (edge == 1) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) e[i] = fast_exp2(fmaf(s[sub][q][i], sc, -lv[i]) + diag[sub][q][i]);
+          for (int i = 0; i < 4; ++i) {
+            const bool keep = i >= q * kTile + (lane & 15) - sub * kTile - g4;
+            e[i] = fast_exp2(keep ? fmaf(s[sub][q][i], sc, -lv[i]) : -INFINITY);
+          }
         } else {
           // query row base + i counts iff lo <= i < hi (causal, inside the prompt,
           // and the last row only for the naive policy); masked terms get the
@@ -712,25 +732,36 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   };
   // uniform: the wavefront has keys and the chunk has a query at or after its first key
   auto active = [&](int ch) { return ch < nch && w_last >= j0 && (ch + 1) * CT::QC - 1 >= j0; };
-  auto stage = [&](int ch, f32x4 (&cur)[2][QS], float4 (&lcur)[2], f32x4 (&nxt)[2][QS], float4 (&lnxt)[2])
-                   __attribute__((always_inline)) {
+  // One pipeline stage, ordered as in the row statistics: the fragments of
+  // chunk ch + 1 are read from LDS, the exponentials of chunk ch (its lse
+  // values read at the end of the stage before) follow, then the MFMAs of
+  // chunk ch + 1 into the same S registers, and last the lse values of chunk
+  // ch + 1 into the registers the exponentials have just released.  The LDS
+  // reads are unconditional (the buffers always hold some chunk): with one path
+  // through them the exponentials wait for the lse values alone, not for the
+  // fragment reads behind them.
+  auto stage = [&](int ch, f32x4 (&s)[2][QS], float4 (&lq)[2]) __attribute__((always_inline)) {
     const int c0 = ch * CT::QC;
+    const bool cur = active(ch), next = active(ch + 1);
     if (ch + 2 < nch) fetch(ch + 2);
-    if (active(ch + 1)) mult(ch + 1, nxt, lnxt);
-    if (active(ch)) {
+    Frag<T, D> fq[2];
+    read(ch + 1, fq);
+    if (cur) {
       if (last_only || c0 + CT::QC > P)
-        soft(std::integral_constant<int, 2>{}, ch, cur, lcur);
+        soft(std::integral_constant<int, 2>{}, ch, s, lq);
       else if (c0 < j0 + CT::ROWS - 1)
-        soft(std::integral_constant<int, 1>{}, ch, cur, lcur);
+        soft(std::integral_constant<int, 1>{}, ch, s, lq);
       else
-        soft(std::integral_constant<int, 0>{}, ch, cur, lcur);
+        soft(std::integral_constant<int, 0>{}, ch, s, lq);
     }
+    if (next) mult(fq, s);
+    read_lse(ch + 1, lq);
     if (ch + 2 < nch) stash((ch - ch0) & 1);  // chunk ch + 2 replaces chunk ch, read one stage ago
     __syncthreads();
   };
 
-  f32x4 sa[2][QS], sb[2][QS];
-  float4 la[2], lb[2];
+  f32x4 s[2][QS];
+  float4 lq[2];
   fetch(ch0);
   stash(0);
   if (ch0 + 1 < nch) {
@@ -738,12 +769,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     stash(1);
   }
   __syncthreads();
-  if (active(ch0)) mult(ch0, sa, la);
-  __syncthreads();  // every wavefront has read the first chunk before the third replaces it
-  for (int ch = ch0; ch < nch; ch += 2) {
-    stage(ch, sa, la, sb, lb);
-    if (ch + 1 < nch) stage(ch + 1, sb, lb, sa, la);
+  if (active(ch0)) {
+    Frag<T, D> fq[2];
+    read(ch0, fq);
+    mult(fq, s);
   }
+  read_lse(ch0, lq);
+  __syncthreads();  // every wavefront has read the first chunk before the third replaces it
+  for (int ch = ch0; ch < nch; ++ch) stage(ch, s, lq);
 #pragma unroll
   for (int q = 0; q < QS; ++q) {
     float c = cs[q];
