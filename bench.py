@@ -50,6 +50,9 @@ def alg_bytes_per_step(wl, cache="input"):
             + U * (2 * d * e + 8) + U * 4)
 
 
+PREFILL_CALLS = 7  # warm prefills timed one by one; the median is reported
+
+
 def prefill_flops(wl):
     """Causal QK^T of the prompt: P(P+1)/2 dot products of length d per unit."""
     P = wl.prompt
@@ -294,25 +297,27 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
                      wl.scale, device=dev, decode_waves=waves, decode_split=split, cache=cache,
                      policy=policy, steps_mode="per_step")
     stream = torch.cuda.current_stream()
-    # The first prefill also loads the kernels' code objects; the second one,
-    # which rebuilds the same state from the same prompt, is the one timed.
-    cache.prefill(*prompt)
-    torch.cuda.synchronize()
+    # The first prefill also loads the kernels' code objects; the warm ones that
+    # follow, each rebuilding the same state from the same prompt, are timed
+    # one by one and the median is reported (one call varies with the clock).
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    p0.record(stream)
-    cache.prefill(*prompt)
-    p1.record(stream)
-    torch.cuda.synchronize()
-    prefill_ms = p0.elapsed_time(p1)
-    # The prefill that also returns the prompt's attention output, warm, then timed.
+
+    def median_prefill_ms(**kw):
+        cache.prefill(*prompt, **kw)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(PREFILL_CALLS):
+            p0.record(stream)
+            cache.prefill(*prompt, **kw)
+            p1.record(stream)
+            torch.cuda.synchronize()
+            times.append(p0.elapsed_time(p1))
+        return sorted(times)[len(times) // 2]
+
+    prefill_ms = median_prefill_ms()
+    # The prefill that also returns the prompt's attention output.
     prompt_out = torch.empty((wl.batch, wl.heads, wl.prompt, wl.head_dim), dtype=torch.float32, device=dev)
-    cache.prefill(*prompt, out=prompt_out)
-    torch.cuda.synchronize()
-    p0.record(stream)
-    cache.prefill(*prompt, out=prompt_out)
-    p1.record(stream)
-    torch.cuda.synchronize()
-    prefill_out_ms = p0.elapsed_time(p1)
+    prefill_out_ms = median_prefill_ms(out=prompt_out)
     del prompt_out
     # torch's own causal flash attention over the same prompt, for context (not in
     # counter runs, whose only copies calibrate the byte counters)
@@ -529,6 +534,7 @@ def main():
         },
         "prefill": {
             "ms": g["prefill_ms"],
+            "timing": f"median of {PREFILL_CALLS} warm calls",
             "qk_tflops": prefill_flops(wl) / (g["prefill_ms"] * 1e-3) / 1e12,
             "peak_tflops": PEAK_BF16_TFLOPS if wl.kv_dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS,
             "frac": prefill_flops(wl) / (g["prefill_ms"] * 1e-3) / 1e12 /
