@@ -580,27 +580,60 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
     }
     return ns;
   };
-  // The prefetched slots: all logits are read before any new score is written
-  // back, so the LDS reads are in flight together; the new scores stay in
-  // registers for the stores below.
+  // The prefetched slots, without per-lane branches (every wavefront runs this
+  // tail at once when the units stream in lockstep): all logits are read before
+  // any new score is written back, so the LDS reads are in flight together;
+  // lanes past n_live read the token's logit and stay out of the argmin.  When
+  // every round has a live slot the rounds form one basic block; otherwise the
+  // rounds past n_live are skipped by a uniform test.  The new scores stay in
+  // registers for the stores below; only the ring row's goes to LDS, where
+  // thread 0 reads it for the row leaving the window.
   float ns_pf[PF];
+  float ring_ns = 0.f;
+  auto pf_rounds = [&](auto all_live) __attribute__((always_inline)) {
+    constexpr bool kAll = decltype(all_live)::value;
 #pragma unroll
-  for (int i = 0; i < PF; ++i) {
-    const int j = tid + i * NT;
-    ns_pf[i] = j < v.n_live ? s_logit[j] : 0.f;
-  }
+    for (int i = 0; i < PF; ++i)
+      ns_pf[i] = kAll || i * NT < v.n_live ? s_logit[min(tid + i * NT, v.n_live)] : 0.f;
 #pragma unroll
-  for (int i = 0; i < PF; ++i) {
-    const int j = tid + i * NT;
-    if (j < v.n_live) {
-      if constexpr (SL) {
+    for (int i = 0; i < PF; ++i) {
+      if (!kAll && i * NT >= v.n_live) break;  // uniform
+      const int j = tid + i * NT;
+      const bool live = j < v.n_live;
+      const int s = v.slot_of(j);
+      const bool cand = live && v.is_cand(s);
+      const float ns = (naive ? 0.f : sc_pf[i]) + fast_exp2(ns_pf[i] - M) * invL;
+      ns_pf[i] = ns;
+      ring_ns = j == v.ring_slot ? ns : ring_ns;
+      const unsigned long long key = ((unsigned long long)__float_as_uint(ns) << 32) | (uint32_t)ps_pf[i];
+      const bool take = cand && key < best;
+      best = take ? key : best;
+      best_slot = take ? s : best_slot;
+    }
+  };
+  if constexpr (SL) {
+    // Scores and positions in LDS (multi-step kernels), read per live slot:
+    // there the tail of one unit overlaps the streaming of others.
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int j = tid + i * NT;
+      ns_pf[i] = j < v.n_live ? s_logit[j] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int j = tid + i * NT;
+      if (j < v.n_live) {
         const int s = v.slot_of(j);
         ns_pf[i] = update(j, ns_pf[i], u.score[s], v.is_cand(s) ? u.pos[s] : 0);
-      } else {
-        ns_pf[i] = update(j, ns_pf[i], sc_pf[i], ps_pf[i]);
       }
     }
+  } else if (v.n_live > (PF - 1) * NT) {
+    pf_rounds(std::true_type{});
+  } else {
+    pf_rounds(std::false_type{});
   }
+  if (!SL && v.ring_slot >= 0 && v.ring_slot < v.n_live && v.ring_slot < PF * NT && v.ring_slot % NT == tid)
+    s_logit[v.ring_slot] = ring_ns;
   // Slots past the prefetched ones (budgets above PF * NT): their scores and
   // positions are loaded kRest at a time before any is used, one memory round
   // trip per batch instead of per slot (the argmin over unique keys does not
@@ -1117,13 +1150,22 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
     pm = collect(up + (size_t)tid * (D + 2));
     pl = collect(up + (size_t)tid * (D + 2) + 1);
   }
-  // All logits (indices clamped to the last one; only those below n_att are kept).
-  for (int j0 = tid; j0 < v.n_att; j0 += kBatch * NT) {
-    float lv[kBatch];
+  // The first kBatch partials' outputs of column tid, in flight with the rest.
+  float ov0[kBatch];
+  if (tid < D) {
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) lv[i] = collect(lg + min(j0 + i * NT, v.n_att - 1));
+    for (int i = 0; i < kBatch; ++i) ov0[i] = collect(up + (size_t)min(i, S - 1) * (D + 2) + 2 + tid);
+  }
+  // All logits (indices clamped to the last one; only those below n_att are
+  // kept), kLogits per thread per round: the k + 1 logits of a budget k up to
+  // kLogits * NT - 1 (4607 with 8 wavefronts) take one round trip.
+  constexpr int kLogits = kBatch + 1;
+  for (int j0 = tid; j0 < v.n_att; j0 += kLogits * NT) {
+    float lv[kLogits];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i)
+    for (int i = 0; i < kLogits; ++i) lv[i] = collect(lg + min(j0 + i * NT, v.n_att - 1));
+#pragma unroll
+    for (int i = 0; i < kLogits; ++i)
       if (j0 + i * NT < v.n_att) s_logit[j0 + i * NT] = lv[i];
   }
   if (tid < S) {
@@ -1157,7 +1199,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
     for (int c0 = 0; c0 < S; c0 += kBatch) {
       float ov[kBatch];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) ov[i] = collect(up + (size_t)min(c0 + i, S - 1) * (D + 2) + 2 + d);
+      for (int i = 0; i < kBatch; ++i)
+        ov[i] = d == tid && c0 == 0 ? ov0[i] : collect(up + (size_t)min(c0 + i, S - 1) * (D + 2) + 2 + d);
 #pragma unroll
       for (int i = 0; i < kBatch; ++i)
         if (c0 + i < S) acc = fmaf(ov[i], fast_exp2(s_pm[c0 + i] - M), acc);
