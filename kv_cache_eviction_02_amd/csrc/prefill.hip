@@ -27,9 +27,14 @@
 // chunk's MFMAs.
 //
 // MFMA use: v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (f32).
-// Lane l supplies row l % 16 of a 16-row tile and the contiguous quarter
-// [(l / 16) * d / 4, (l / 16 + 1) * d / 4) of the head dimension; A and B use
-// the same split, so every product q_c * k_c is formed exactly once.  The
+// Lane l supplies row l % 16 of a 16-row tile; of each 64-byte piece i of the
+// row it supplies the 16 bytes at 64 i + 16 (l / 16), the i-th 16-byte chunk of
+// its fragment.  A and B use the same split, so every product q_c * k_c is
+// formed exactly once.  In LDS, rows are ROWB + 32 bytes apart: with that
+// stride and this split the 16 rows of a subtile read by one ds_read_b128 fall
+// on distinct banks (measured on gfx950: no bank-conflict cycles, where the
+// contiguous-quarter split at a ROWB + 16 stride spent half the LDS cycles in
+// conflicts).  The
 // 16x16 result lands as acc[i] = dot(moving row 4 * (l / 16) + i, fixed row l % 16).
 #include <float.h>
 #include <math.h>
@@ -49,19 +54,18 @@ constexpr int kTile = 16;
 
 template <typename T, int D>
 struct Frag {
-  static constexpr int kBytes = D / 4 * Elem<T>::kBytes;  // per lane: a quarter row
+  static constexpr int kBytes = D / 4 * Elem<T>::kBytes;  // per lane: a quarter of the row
   static constexpr int kChunks = kBytes / 16;
   static_assert(kChunks * 16 == kBytes, "quarter row must be whole 16-byte chunks");
   uint4 c[kChunks];
 
-  // Row `row0 + lane % 16` of a [n, D] matrix, quarter lane / 16; zero past n.
+  // Row `row0 + lane % 16` of a [n, D] matrix, chunks 64 i + 16 (lane / 16); zero past n.
   __device__ inline void load(const char* base, int row0, int n, int lane) {
     const int row = row0 + (lane & 15);
-    const int quarter = lane >> 4;
     if (row < n) {
-      const char* p = base + (size_t)row * (D * Elem<T>::kBytes) + quarter * kBytes;
+      const char* p = base + (size_t)row * (D * Elem<T>::kBytes) + (lane >> 4) * 16;
 #pragma unroll
-      for (int i = 0; i < kChunks; ++i) c[i] = load16(p + 16 * i);
+      for (int i = 0; i < kChunks; ++i) c[i] = load16(p + 64 * i);
     } else {
 #pragma unroll
       for (int i = 0; i < kChunks; ++i) c[i] = make_uint4(0, 0, 0, 0);
@@ -73,9 +77,9 @@ struct Frag {
   // must be masked by the caller.
   __device__ inline void load_clamped(const char* base, int row0, int n, int lane) {
     const int row = min(row0 + (lane & 15), n - 1);
-    const char* p = base + (size_t)row * (D * Elem<T>::kBytes) + (lane >> 4) * kBytes;
+    const char* p = base + (size_t)row * (D * Elem<T>::kBytes) + (lane >> 4) * 16;
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) c[i] = load16(p + 16 * i);
+    for (int i = 0; i < kChunks; ++i) c[i] = load16(p + 64 * i);
   }
 };
 
@@ -146,7 +150,7 @@ struct AttendTile {
   static constexpr int BQ = kWaves * ROWS;            // queries per block
   static constexpr int KC = 2 * kTile;                // keys per chunk
   static constexpr int ROWB = D * Elem<T>::kBytes;
-  static constexpr int KSTR = ROWB + 16;              // K rows in LDS: 16 rows of one subtile hit distinct banks
+  static constexpr int KSTR = ROWB + 32;              // K rows in LDS: 16 rows of one subtile hit distinct banks
   static constexpr int VSTR = ROWB + 32;              // V rows in LDS: 8 rows x 32 bytes hit distinct banks
   static constexpr int PIECES = KC * ROWB / 16;       // 16-byte pieces of a K (or V) chunk
   static constexpr int PER_T = (PIECES + kWaves * 64 - 1) / (kWaves * 64);
@@ -165,12 +169,12 @@ __device__ inline uint4 zero_unless(bool keep, uint4 x) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Rows row0 .. row0 + 15 of a K chunk in LDS as MFMA operands (lane: row l%16, quarter l/16).
+// Rows row0 .. row0 + 15 of a chunk in LDS as MFMA operands (lane: row l%16, chunks 64 i + 16 (l/16)).
 template <typename T, int D>
 __device__ inline void load_lds_frag(Frag<T, D>& f, const char* base, int row0, int stride, int lane) {
-  const char* p = base + (row0 + (lane & 15)) * stride + (lane >> 4) * Frag<T, D>::kBytes;
+  const char* p = base + (row0 + (lane & 15)) * stride + (lane >> 4) * 16;
 #pragma unroll
-  for (int i = 0; i < Frag<T, D>::kChunks; ++i) f.c[i] = *reinterpret_cast<const uint4*>(p + 16 * i);
+  for (int i = 0; i < Frag<T, D>::kChunks; ++i) f.c[i] = *reinterpret_cast<const uint4*>(p + 64 * i);
 }
 
 template <typename T, int D>
@@ -397,7 +401,7 @@ struct RowTile {
   static constexpr int BQ = kWaves * ROWS;
   static constexpr int KC = 2 * kTile;
   static constexpr int ROWB = D * Elem<T>::kBytes;
-  static constexpr int KSTR = ROWB + 16;
+  static constexpr int KSTR = ROWB + 32;  // 16 rows of one subtile hit distinct banks
   static constexpr int PIECES = KC * ROWB / 16;
   static constexpr int PER_T = (PIECES + kWaves * 64 - 1) / (kWaves * 64);
   static constexpr int BUF = KC * KSTR;
@@ -595,7 +599,7 @@ struct ColTile {
   static constexpr int BK = kWaves * ROWS;           // keys per block
   static constexpr int QC = 2 * kTile;               // query rows per chunk
   static constexpr int ROWB = D * Elem<T>::kBytes;
-  static constexpr int QSTR = ROWB + 16;             // 16 rows of one subtile hit distinct banks
+  static constexpr int QSTR = ROWB + 32;             // 16 rows of one subtile hit distinct banks
   static constexpr int PIECES = QC * ROWB / 16;
   static constexpr int PER_T = (PIECES + kWaves * 64 - 1) / (kWaves * 64);
   static constexpr int BUF = QC * QSTR + QC * 4;     // query rows + their lse
