@@ -160,6 +160,7 @@ struct AttendTile {
 };
 
 constexpr float kLazy = 8.f;
+constexpr float kRescale = 0x1p64f;  // row statistics: largest chunk sum taken without a rescale
 
 // x, or zeros when !keep (a value select: no branch, no address select).
 __device__ inline uint4 zero_unless(bool keep, uint4 x) {
@@ -379,8 +380,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 // the wavefronts).  At chunk c a wavefront issues the MFMAs of chunk c + 1 and
 // then runs the exponentials of chunk c from registers, so the matrix and
 // vector pipes overlap inside the wavefront.  The running maximum is kept per
-// lane group and raised only when a chunk exceeds it by more than kLazy; the
-// four lane groups of a query merge their (max, sum) at the end.
+// lane group and raised only when a chunk's sum against it would exceed
+// kRescale; the four lane groups of a query merge their (max, sum) at the end.
 #ifndef H2O_ROW_QS
 #define H2O_ROW_QS 2
 #endif
@@ -507,21 +508,37 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
           for (int i = 0; i < 4; ++i) s[sub][q][i] += diag[q][sub][i];
     }
+    // Exponentials against the running maximum m[q] without first taking the
+    // chunk's maximum.  A lane whose chunk sum exceeds 2^64 (or is infinite,
+    // as on its first chunk, where m[q] is kLow) raises m[q] to the chunk's
+    // maximum and takes the chunk again: rare, and a uniform branch.  Every
+    // term then stays below 2^64 and one term of the sum is at least 1 (the one
+    // that set m[q]), so the float sum keeps its relative precision, and no
+    // sum over a row overflows.
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
-      float mx = fmaxf(s[0][q][0], s[0][q][1]);
-      mx = fmaxf(fmaxf(mx, s[0][q][2]), s[0][q][3]);
-      mx = fmaxf(fmaxf(mx, s[1][q][0]), s[1][q][1]);
-      mx = fmaxf(fmaxf(mx, s[1][q][2]), s[1][q][3]);
-      const float ms = mx * sc;
-      const float mn = ms > m[q] + kLazy ? ms : m[q];
-      const float alpha = fast_exp2(m[q] - mn);
-      m[q] = mn;
       float e[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(s[i >> 2][q][i & 3], sc, -mn));
-      const float add = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-      l[q] = fmaf(l[q], alpha, add);
+      for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(s[i >> 2][q][i & 3], sc, -m[q]));
+      float add = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      const bool big = !(add <= kRescale);
+      if (__builtin_amdgcn_ballot_w64(big)) {  // uniform
+        float mx = fmaxf(s[0][q][0], s[0][q][1]);
+        mx = fmaxf(fmaxf(mx, s[0][q][2]), s[0][q][3]);
+        mx = fmaxf(fmaxf(mx, s[1][q][0]), s[1][q][1]);
+        mx = fmaxf(fmaxf(mx, s[1][q][2]), s[1][q][3]);
+        const float mn = big ? fmaxf(m[q], mx * sc) : m[q];
+        const float alpha = fast_exp2(m[q] - mn);
+        m[q] = mn;
+        if (big) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(s[i >> 2][q][i & 3], sc, -mn));
+          add = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        }
+        l[q] = fmaf(l[q], alpha, add);
+      } else {
+        l[q] += add;
+      }
     }
   };
   auto active = [&](int ch) { return ch < nch && ch * RT::KC <= qw_last; };  // uniform
