@@ -181,11 +181,24 @@ struct Stash {
   uint4 ring[2][GG::LPR];  // K, V of the ring slot leaving the window
   uint4 self[2][GG::LPR];  // K, V of the decoded token (cache format; not used for E4M3)
   float ring_scale[2];     // E4M3 row scales of the ring row
-  // E4M3: the decoded token's exact input rows, kept from the stream's first
-  // read of them for the quantized admission (a re-read at the end of a long
-  // stream would come from memory)
-  uint4 tok[2][GG::kQuant ? GG::IROWB / 16 : 1];
+  // E4M3: the decoded token's K and V codes and row scales, computed where the
+  // stream first reads its exact rows, for the admission at the end of the step
+  uint4 tokq[2][GG::kQuant ? GG::LPR : 1];
+  float tok_scale[2];
 };
+
+// E4M3 codes of a lane's 16 values of a row, and the row scale amax / 448 with
+// amax taken over the lane's group of G lanes (lanes with act false hold no
+// part of the row).
+template <typename GG>
+__device__ inline uint4 quantize_chunk(const float* x, bool act, float& scale) {
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < GG::EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  amax = group_max<GG::G>(act ? amax : 0.f);
+  scale = __fdiv_rn(amax, 448.f);
+  return quantize16_e4m3(x, amax);
+}
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4_t lds_v4;
@@ -239,11 +252,16 @@ __device__ __forceinline__ void unpack_input(const uint4* c, float* x) {
 // also for up to DEPTH - 1 batches past hi (the callers' fetch re-reads a valid
 // row there), so every index into the register ring is a compile-time
 // constant; consumption stops at the first batch past hi (a wave-uniform exit).
-template <int DEPTH, int NG, typename Buf, typename F, typename C>
-__device__ __forceinline__ void row_pipeline(int lo, int hi, F&& fetch, C&& consume) {
+// `start` runs once the first batches are in flight, before any is consumed.
+struct NoStart {
+  __device__ void operator()() const {}
+};
+template <int DEPTH, int NG, typename Buf, typename F, typename C, typename S = NoStart>
+__device__ __forceinline__ void row_pipeline(int lo, int hi, F&& fetch, C&& consume, S&& start = S{}) {
   Buf b[DEPTH];
 #pragma unroll
   for (int i = 0; i + 1 < DEPTH; ++i) fetch(lo + i * NG, b[i]);
+  start();
   for (int base = lo; base < hi; base += DEPTH * NG) {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
@@ -352,46 +370,51 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
     row_pipeline<DEPTH, NG, RowBuf>(lo, hi, fetch, consume);
   } else {
     // The decoded token (exact bf16 row) seeds row group 0 when it is in range.
-    if (v.n_live >= lo && v.n_live < hi) {
-      float kx[EPL];
+    // Its rows are loaded with the first row batch, and the seed runs while that
+    // batch is in flight; its arithmetic is unconditional (results kept by a
+    // select), so the loads stay ahead of every wait.
+    const bool seed = v.n_live >= lo && v.n_live < hi;  // uniform
+    uint4 tkr[GG::ICH], tvr[GG::ICH];
+    if constexpr (!RES) {
+#pragma unroll
+      for (int i = 0; i < GG::ICH; ++i) {
+        tkr[i] = load16(u.kn + (chunk * GG::ICH + i) * 16);
+        tvr[i] = load16(u.vn + (chunk * GG::ICH + i) * 16);
+      }
+    }
+    auto seed_group0 = [&]() __attribute__((always_inline)) {
+      float kx[EPL], vx[EPL];
       if constexpr (RES) {
         unpack_input<GG>(in->k, kx);
+        unpack_input<GG>(in->v, vx);
       } else {
-        uint4 raw[GG::ICH];
-#pragma unroll
-        for (int i = 0; i < GG::ICH; ++i) raw[i] = load16(u.kn + (chunk * GG::ICH + i) * 16);
-        unpack_input<GG>(raw, kx);
-        if (grp == 0 && act) {
-#pragma unroll
-          for (int i = 0; i < GG::ICH; ++i) st->tok[0][chunk * GG::ICH + i] = raw[i];
-        }
+        unpack_input<GG>(tkr, kx);
+        unpack_input<GG>(tvr, vx);
       }
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) d = fmaf(qf[e], kx[e], d);
       d = group_sum<G>(d);
       const float ls = d * scale_log2;
-      if (grp == 0) {
-        if (gl == 0) s_logit[v.n_live] = ls;
-        float vx[EPL];
-        if constexpr (RES) {
-          unpack_input<GG>(in->v, vx);
-        } else {
-          uint4 raw[GG::ICH];
-#pragma unroll
-          for (int i = 0; i < GG::ICH; ++i) raw[i] = load16(u.vn + (chunk * GG::ICH + i) * 16);
-          unpack_input<GG>(raw, vx);
-          if (act) {
-#pragma unroll
-            for (int i = 0; i < GG::ICH; ++i) st->tok[1][chunk * GG::ICH + i] = raw[i];
-          }
+      const bool own = seed && grp == 0;
+      if (own && gl == 0) s_logit[v.n_live] = ls;
+      // The token's codes for the admission, while the first batch is in
+      // flight: every row group holds both rows; groups 0 and 1 (lanes [0, G)
+      // and [G, 2G) of wave 0) quantize K and V.
+      if (seed && threadIdx.x < 64) {  // uniform
+        const int w = grp == 1 ? 1 : 0;
+        float sc;
+        const uint4 codes = quantize_chunk<GG>(w ? vx : kx, act, sc);
+        if (grp < 2) {
+          if (act) st->tokq[w][chunk] = codes;
+          if (gl == 0) st->tok_scale[w] = sc;
         }
-        m = ls;
-        lsum = 1.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = act ? vx[e] : 0.f;
       }
-    }
+      m = own ? ls : m;
+      lsum = own ? 1.f : lsum;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = own ? (act ? vx[e] : 0.f) : o[e];
+    };
     const int end = min(hi, v.n_live);  // cached rows only
     auto fetch = [&](int base, QuantRowBuf& b) {
       const int j = base + grp;
@@ -454,7 +477,7 @@ __device__ __forceinline__ void stream_rows(const StepView& v, const UnitPtrs<GG
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] = fmaf(pv, vf[e], o[e]);
     };
-    row_pipeline<DEPTH, NG, QuantRowBuf>(lo, end, fetch, consume);
+    row_pipeline<DEPTH, NG, QuantRowBuf>(lo, end, fetch, consume, seed_group0);
   }
 }
 
@@ -496,53 +519,61 @@ __device__ __forceinline__ GroupMerge<GG::NG> merge_groups(float m, float lsum, 
   return r;
 }
 
-// Quantize the decoded token's K and V rows into slot `slot` (E4M3 cache):
-// lanes [0, G) of wave 0 take K, lanes [G, 2G) take V, each lane 16 values.
-// The exact rows come from the stash (TOK == 1), from the lane's own step
-// inputs (TOK == 2: lane tid holds chunk tid % G of both rows) or from memory
-// (TOK == 0).  With RES the codes and scales also go to the LDS copy of the rows.
-template <typename GG, bool RES = false, int TOK = 0>
-__device__ inline void admit_quantized(const UnitPtrs<GG>& u, int slot, const ResRows<GG>* res = nullptr,
-                                       const Stash<GG>* st = nullptr, const StepIn<GG>* in = nullptr) {
-  constexpr int G = GG::G, LPR = GG::LPR, EPL = GG::EPL;
+// The decoded token's K and V rows into slot `slot` of an E4M3 cache.
+// STASHED: the codes and row scales wait in the LDS stash (computed where the
+// stream first read the token); else lanes [0, G) of wave 0 quantize K and
+// lanes [G, 2G) V from the exact rows in memory.  With RES the codes and
+// scales also go to the LDS copy of the rows.
+template <typename GG, bool RES = false, bool STASHED = true>
+__device__ inline void admit_quantized(const UnitPtrs<GG>& u, int slot, const ResRows<GG>* res,
+                                       const Stash<GG>* st) {
+  constexpr int G = GG::G, LPR = GG::LPR, EPL = GG::EPL, ROWB = GG::ROWB;
   const int tid = threadIdx.x;
-  if (tid >= 2 * G) return;
-  const bool is_v = tid >= G;
-  const int c = tid & (G - 1);
-  const bool act = c < LPR;
-  float x[EPL];
-  if constexpr (TOK == 1) {
-    uint4 raw[GG::ICH];
-#pragma unroll
-    for (int i = 0; i < GG::ICH; ++i) raw[i] = st->tok[is_v ? 1 : 0][(act ? c : 0) * GG::ICH + i];
-    unpack_input<GG>(raw, x);
-  } else if constexpr (TOK == 2) {
-    unpack_input<GG>(is_v ? in->v : in->k, x);
+  if constexpr (STASHED) {
+    if (tid < LPR) {
+      const uint4 kc = st->tokq[0][tid];
+      const uint4 vc = st->tokq[1][tid];
+      store16(u.K + (size_t)slot * ROWB + tid * 16, kc);
+      store16(u.V + (size_t)slot * ROWB + tid * 16, vc);
+      if constexpr (RES) {
+        lds_store16(res->K + slot * ROWB + tid * 16, kc);
+        lds_store16(res->V + slot * ROWB + tid * 16, vc);
+      }
+    }
+    if (tid == 0) {
+      const float ksc = st->tok_scale[0], vsc = st->tok_scale[1];
+      u.ks[slot] = ksc;
+      u.vs[slot] = vsc;
+      if constexpr (RES) {
+        res->ks[slot] = ksc;
+        res->vs[slot] = vsc;
+      }
+    }
   } else {
+    if (tid >= 2 * G) return;
+    const bool is_v = tid >= G;
+    const int c = tid & (G - 1);
+    const bool act = c < LPR;
+    float x[EPL];
     load_input<GG>(is_v ? u.vn : u.kn, act ? c : 0, x);
-  }
-  float amax = 0.f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
-  amax = group_max<G>(act ? amax : 0.f);
-  char* row = (is_v ? u.V : u.K) + (size_t)slot * GG::ROWB;
-  const uint4 codes = quantize16_e4m3(x, amax);
-  const float sc = __fdiv_rn(amax, 448.f);
-  if (act) store16(row + c * 16, codes);
-  if (c == 0) (is_v ? u.vs : u.ks)[slot] = sc;
-  if constexpr (RES) {
-    if (act) lds_store16((is_v ? res->V : res->K) + slot * GG::ROWB + c * 16, codes);
-    if (c == 0) (is_v ? res->vs : res->ks)[slot] = sc;
+    float sc;
+    const uint4 codes = quantize_chunk<GG>(x, act, sc);
+    if (act) store16((is_v ? u.V : u.K) + (size_t)slot * ROWB + c * 16, codes);
+    if (c == 0) (is_v ? u.vs : u.ks)[slot] = sc;
+    if constexpr (RES) {
+      if (act) lds_store16((is_v ? res->V : res->K) + slot * ROWB + c * 16, codes);
+      if (c == 0) (is_v ? res->vs : res->ks)[slot] = sc;
+    }
   }
 }
 
 // Score update, eviction argmin and admission for one unit, given the exact
 // softmax max M and 1/L.  Logits of rows [0, n_att) are in s_logit; the
 // scores this thread owns were prefetched into sc_pf / ps_pf; the ring row and
-// (unquantized caches) the new token's row are in the LDS stash.
-// TOK_STASHED: the stream of this workgroup read the decoded token's rows
-// (E4M3: they are in the stash); the split kernel's combining workgroup may not
-// have, and reads them from memory.
+// the new token's row (E4M3: its codes and scales) are in the LDS stash.
+// TOK_STASHED: the stream of this workgroup read the decoded token's rows and
+// stashed them; the split kernel's combining workgroup may not have, and reads
+// them from memory.
 // SL: the scores and positions are in LDS (u.score / u.pos point there) and
 // are read where they are used instead of being prefetched.
 template <typename GG, bool RES = false, bool TOK_STASHED = true, bool SL = false>
@@ -735,8 +766,8 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
   }
   if constexpr (RES) {
     // Thread tid < LPR moves chunk tid of the rows: the ring row is read from
-    // LDS before the token replaces it, the token's chunk is the lane's own
-    // step input (lane tid holds chunk tid).
+    // LDS before the token replaces it; the token's chunk is the lane's own
+    // step input (lane tid holds chunk tid), or its codes in the stash (E4M3).
     if (tid < LPR && dst >= 0) {
       const uint4 rk = lds_load16(res->K + v.ring_slot * ROWB + tid * 16);
       const uint4 rv = lds_load16(res->V + v.ring_slot * ROWB + tid * 16);
@@ -747,7 +778,7 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
     }
     if (adm >= 0) {
       if constexpr (GG::kQuant) {
-        admit_quantized<GG, RES, 2>(u, adm, res, st, in);
+        admit_quantized<GG, true, true>(u, adm, res, st);
       } else if (tid < LPR) {
         store16(u.K + (size_t)adm * ROWB + tid * 16, in->k[0]);
         store16(u.V + (size_t)adm * ROWB + tid * 16, in->v[0]);
@@ -762,7 +793,7 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
     }
     if (adm >= 0) {
       if constexpr (GG::kQuant) {
-        admit_quantized<GG, false, TOK_STASHED ? 1 : 0>(u, adm, nullptr, st);
+        admit_quantized<GG, false, TOK_STASHED>(u, adm, nullptr, st);
       } else if (tid < LPR) {
         store16(u.K + (size_t)adm * ROWB + tid * 16, st->self[0][tid]);
         store16(u.V + (size_t)adm * ROWB + tid * 16, st->self[1][tid]);
@@ -771,19 +802,31 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
   }
 }
 
-// Prefetch of the scores a thread will update, and of the candidates' positions.
-template <typename GG>
+// Prefetch of the scores a thread will update, and of the candidates'
+// positions.  With kAll the loads are unconditional (threads past the live
+// slots read slot 0's score, threads of other slots slot 0's position, and
+// ignore them), so they all go out at once and the compiler counts them
+// exactly: the split decode's combining workgroup issues them that way with
+// its partials' loads.  The per-step kernels measured slightly faster with
+// guarded loads.
+template <typename GG, bool kAll = false>
 __device__ __forceinline__ void prefetch_scores(const StepView& v, const UnitPtrs<GG>& u, float* sc_pf,
                                                 int* ps_pf) {
 #pragma unroll
   for (int i = 0; i < GG::PF; ++i) {
     const int j = threadIdx.x + i * GG::NT;
-    sc_pf[i] = 0.f;
-    ps_pf[i] = 0;
-    if (j < v.n_live) {
-      const int s = v.slot_of(j);
+    if constexpr (kAll) {
+      const int s = j < v.n_live ? v.slot_of(j) : 0;
       sc_pf[i] = u.score[s];
-      if (v.is_cand(s)) ps_pf[i] = u.pos[s];
+      ps_pf[i] = u.pos[v.is_cand(s) ? s : 0];
+    } else {
+      sc_pf[i] = 0.f;
+      ps_pf[i] = 0;
+      if (j < v.n_live) {
+        const int s = v.slot_of(j);
+        sc_pf[i] = u.score[s];
+        if (v.is_cand(s)) ps_pf[i] = u.pos[s];
+      }
     }
   }
 }
@@ -1123,7 +1166,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a, Spl
   // with the partials'.
   float sc_pf[PF];
   int ps_pf[PF];
-  prefetch_scores<GG>(v, u, sc_pf, ps_pf);
+  prefetch_scores<GG, true>(v, u, sc_pf, ps_pf);
   // The rows the admission writes (still intact: only this workgroup writes
   // the unit's state) and the partials' maxima and sums go into registers
   // first, in flight with the logits, and into LDS after them.
