@@ -231,6 +231,19 @@ struct StepIn {
   uint4 v[GG::ICH];
 };
 
+// Uses the loaded registers of `in` here, so the compiler waits for their loads
+// at this point rather than at their first later use.
+template <typename GG>
+__device__ __forceinline__ void settle(StepIn<GG>& in) {
+  auto one = [](uint4& x) { asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w)); };
+#pragma unroll
+  for (int i = 0; i < GG::ICH; ++i) {
+    one(in.q[i]);
+    one(in.k[i]);
+    one(in.v[i]);
+  }
+}
+
 template <typename GG>
 __device__ __forceinline__ void load_step_in(const UnitPtrs<GG>& u, int chunk, StepIn<GG>& in) {
 #pragma unroll
@@ -766,8 +779,8 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
   }
   if constexpr (RES) {
     // Thread tid < LPR moves chunk tid of the rows: the ring row is read from
-    // LDS before the token replaces it; the token's chunk is the lane's own
-    // step input (lane tid holds chunk tid), or its codes in the stash (E4M3).
+    // LDS before the token replaces it; the token's rows are LDS row k (their
+    // codes in the stash for E4M3).
     if (tid < LPR && dst >= 0) {
       const uint4 rk = lds_load16(res->K + v.ring_slot * ROWB + tid * 16);
       const uint4 rv = lds_load16(res->V + v.ring_slot * ROWB + tid * 16);
@@ -780,10 +793,12 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
       if constexpr (GG::kQuant) {
         admit_quantized<GG, true, true>(u, adm, res, st);
       } else if (tid < LPR) {
-        store16(u.K + (size_t)adm * ROWB + tid * 16, in->k[0]);
-        store16(u.V + (size_t)adm * ROWB + tid * 16, in->v[0]);
-        lds_store16(res->K + adm * ROWB + tid * 16, in->k[0]);
-        lds_store16(res->V + adm * ROWB + tid * 16, in->v[0]);
+        const uint4 tk = lds_load16(res->K + v.k * ROWB + tid * 16);
+        const uint4 tv = lds_load16(res->V + v.k * ROWB + tid * 16);
+        store16(u.K + (size_t)adm * ROWB + tid * 16, tk);
+        store16(u.V + (size_t)adm * ROWB + tid * 16, tv);
+        lds_store16(res->K + adm * ROWB + tid * 16, tk);
+        lds_store16(res->V + adm * ROWB + tid * 16, tv);
       }
     }
   } else {
@@ -846,11 +861,12 @@ struct StepShared {
 // n_live + 1 floats.  score_lds / pos_lds: when not null, the unit's scores and
 // positions live in LDS (k entries each) instead of the state buffers.
 // With RES the cached rows are read from the LDS copy `res` (kept current by
-// the admission) and the step's inputs come from `in`.
-template <typename GG, int D, bool RES = false, bool SL = false>
+// the admission) and the step's inputs come from `in`, which is not read after
+// the row stream; `streamed` runs there.
+template <typename GG, int D, bool RES = false, bool SL = false, typename H = NoStart>
 __device__ __forceinline__ void unit_step(const DecodeArgs& a, int unit, StepShared<GG, D>& sh, float* s_logit,
                                           float* score_lds, int32_t* pos_lds, const ResRows<GG>* res = nullptr,
-                                          const StepIn<GG>* in = nullptr) {
+                                          const StepIn<GG>* in = nullptr, H&& streamed = H{}) {
   constexpr int EPL = GG::EPL, LPR = GG::LPR, NG = GG::NG, NT = GG::NT, PF = GG::PF;
   const int tid = threadIdx.x;
   const StepView v(a);
@@ -883,6 +899,7 @@ __device__ __forceinline__ void unit_step(const DecodeArgs& a, int unit, StepSha
     stream_rows<GG, 2, true>(v, u, 0, v.n_att, qf, a.scale_log2, s_logit, &sh.st, m, lsum, o, res, in);
   else
     stream_rows<GG>(v, u, 0, v.n_att, qf, a.scale_log2, s_logit, &sh.st, m, lsum, o);
+  streamed();
 
   const GroupMerge<NG> gm = merge_groups<GG, D>(m, lsum, o, sh.s_o, sh.s_m, sh.s_l);
   const float invL = 1.f / gm.L;
@@ -1045,23 +1062,32 @@ __global__ __launch_bounds__(NW * 64) void decode_resident_kernel(DecodeArgs a, 
     as.v_new = (const char*)a.v_new + st * in_step;
     as.out = a.out + (size_t)st * a.units * D;
     as.evicted = a.evicted ? a.evicted + (size_t)st * a.units : nullptr;
-    if (st + 1 < n_steps) {
+    const bool more = st + 1 < n_steps;
+    {
+      // the next step's inputs (the last step re-reads its own: every path loads)
+      const size_t adv = more ? in_step : 0;
       DecodeArgs an = as;
-      an.q = (const char*)as.q + in_step;
-      an.k_new = (const char*)as.k_new + in_step;
-      an.v_new = (const char*)as.v_new + in_step;
+      an.q = (const char*)as.q + adv;
+      an.k_new = (const char*)as.k_new + adv;
+      an.v_new = (const char*)as.v_new + adv;
       load_step_in<GG>(UnitPtrs<GG>(an, unit, k), chunk, nxt);
     }
-    unit_step<GG, D, true, true>(as, unit, sh, s_logit, s_score, s_pos, &res, &cur);
+    // They move into `cur` once this step's rows are streamed, long after their
+    // loads arrived; left to the first use at the end of the step, the wait
+    // for them would also wait for the acknowledgement of the step's stores.
+    unit_step<GG, D, true, true>(as, unit, sh, s_logit, s_score, s_pos, &res, &cur, [&]() {
+      settle(nxt);
+      cur = nxt;
+    });
     if constexpr (XR) {
-      // the next token's row; every read of row k in this step is behind the merge barrier
-      if (st + 1 < n_steps && tid < GG::LPR) {
-        lds_store16(res.K + k * ROWB + tid * 16, nxt.k[0]);
-        lds_store16(res.V + k * ROWB + tid * 16, nxt.v[0]);
+      // the next token's row; every read of row k in this step (the stream, and
+      // the admission by these same threads) comes before
+      if (more && tid < GG::LPR) {
+        lds_store16(res.K + k * ROWB + tid * 16, cur.k[0]);
+        lds_store16(res.V + k * ROWB + tid * 16, cur.v[0]);
       }
     }
     __syncthreads();
-    cur = nxt;
   }
   for (int i = tid; i < k; i += NT) {
     a.score[ubase + i] = s_score[i];
