@@ -102,6 +102,33 @@ __device__ inline float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+// Every lane l gets its own value of x and lane l ^ 16's (pair16) or lane
+// l ^ 32's (pair32), in an order that depends on the lane: gfx950's
+// v_permlane16_swap / v_permlane32_swap exchange rows between two copies of x
+// in the vector ALU, where a shuffle (ds_bpermute) takes an LDS round trip.
+// Symmetric operations of the pair (sum, min, max) need not know the order.
+struct LanePair {
+  uint32_t a, b;
+};
+__device__ inline LanePair pair16(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return {r[0], r[1]};
+}
+__device__ inline LanePair pair32(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return {r[0], r[1]};
+}
+template <bool k32>
+__device__ inline float sum_pair(float x) {
+  const LanePair p = k32 ? pair32(__float_as_uint(x)) : pair16(__float_as_uint(x));
+  return __uint_as_float(p.a) + __uint_as_float(p.b);
+}
+template <bool k32>
+__device__ inline float max_pair(float x) {
+  const LanePair p = k32 ? pair32(__float_as_uint(x)) : pair16(__float_as_uint(x));
+  return fmaxf(__uint_as_float(p.a), __uint_as_float(p.b));
+}
+
 // Sum over aligned groups of G consecutive lanes; every lane of a group gets the total.
 template <int G>
 __device__ inline float group_sum(float x) {
@@ -110,8 +137,8 @@ __device__ inline float group_sum(float x) {
   x += dpp<kDppQuadXor2>(x);
   if constexpr (G >= 8) x += dpp<kDppHalfMirror>(x);
   if constexpr (G >= 16) x += dpp<kDppRowMirror>(x);
-  if constexpr (G >= 32) x += __shfl_xor(x, 16, 64);
-  if constexpr (G >= 64) x += __shfl_xor(x, 32, 64);
+  if constexpr (G >= 32) x = sum_pair<false>(x);
+  if constexpr (G >= 64) x = sum_pair<true>(x);
   return x;
 }
 

@@ -63,10 +63,14 @@ constexpr int ceil_pow2(int x) {
   return p;
 }
 
-__device__ inline unsigned long long shfl_xor_u64(unsigned long long x, int mask) {
-  const uint32_t lo = __shfl_xor((uint32_t)x, mask, 64);
-  const uint32_t hi = __shfl_xor((uint32_t)(x >> 32), mask, 64);
-  return ((unsigned long long)hi << 32) | lo;
+// Minimum of the lane's key and lane l ^ 16's (k32: l ^ 32's), in every lane.
+template <bool k32>
+__device__ inline unsigned long long min_pair_u64(unsigned long long x) {
+  const LanePair lo = k32 ? pair32((uint32_t)x) : pair16((uint32_t)x);
+  const LanePair hi = k32 ? pair32((uint32_t)(x >> 32)) : pair16((uint32_t)(x >> 32));
+  const unsigned long long a = ((unsigned long long)hi.a << 32) | lo.a;
+  const unsigned long long b = ((unsigned long long)hi.b << 32) | lo.b;
+  return a < b ? a : b;
 }
 
 template <int CTRL>
@@ -77,7 +81,8 @@ __device__ inline unsigned long long dpp_u64(unsigned long long x) {
 }
 
 // Minimum over the 64 lanes, in every lane: DPP within each row of 16 lanes
-// (quad swaps, then the half-row and row mirrors), then two cross-row shuffles.
+// (quad swaps, then the half-row and row mirrors), then the two cross-row
+// permlane swaps.
 __device__ inline unsigned long long wave_min_u64(unsigned long long w) {
   unsigned long long o;
   o = dpp_u64<kDppQuadXor1>(w);
@@ -88,10 +93,8 @@ __device__ inline unsigned long long wave_min_u64(unsigned long long w) {
   w = o < w ? o : w;
   o = dpp_u64<kDppRowMirror>(w);
   w = o < w ? o : w;
-  o = shfl_xor_u64(w, 16);
-  w = o < w ? o : w;
-  o = shfl_xor_u64(w, 32);
-  return o < w ? o : w;
+  w = min_pair_u64<false>(w);
+  return min_pair_u64<true>(w);
 }
 
 // T: input element type (q, k_new, v_new); C: cache element type.

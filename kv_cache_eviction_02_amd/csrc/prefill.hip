@@ -284,8 +284,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       mx = fmaxf(fmaxf(mx, s[1][q][0]), s[1][q][1]);
       mx = fmaxf(fmaxf(mx, s[1][q][2]), s[1][q][3]);
       // one maximum for the four lane groups of a query
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max_pair<false>(mx);
+      mx = max_pair<true>(mx);
       const float ms = mx * sc;
       const bool raise = ms > m[q] + kLazy;
       const float mn = raise ? ms : m[q];
@@ -358,8 +358,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
   for (int q = 0; q < QS; ++q) {
     float lt = l[q];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    lt = sum_pair<false>(lt);
+    lt = sum_pair<true>(lt);
     const int qi = qw0 + q * kTile + (lane & 15);
     if (qi < P) {
       const float inv = 1.f / lt;
