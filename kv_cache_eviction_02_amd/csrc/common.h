@@ -90,6 +90,10 @@ __device__ inline uint4 load16_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ inline void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+// Streaming 16-byte store with the non-temporal hint.
+__device__ inline void store16_nt(void* p, const uint4& v) {
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
 
 // DPP lane permutations (row = 16 lanes).
 constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]

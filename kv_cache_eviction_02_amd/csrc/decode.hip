@@ -113,6 +113,10 @@ struct Geo {
   static constexpr int IROWB = D * EI::kBytes;  // input row bytes
   static constexpr int ICH = EPL * EI::kBytes / 16;  // 16-byte input chunks per lane
   static constexpr int PF = 8;               // slots per thread prefetched for the score update
+  // Admitted rows stored with the non-temporal hint at large batch (up to four
+  // wavefronts per unit), where the caches stream far more than they hold; the
+  // small batches' working sets stay in the caches, which the hint bypasses.
+  static constexpr bool kNtRows = NW <= 4;
   static_assert(LPR * EPL == D && G <= 64, "row mapping");
   static_assert(!kQuant || std::is_same<T, bf16>::value, "E4M3 cache takes bf16 inputs");
 };
@@ -213,6 +217,15 @@ __device__ inline uint4 lds_load16(const lds_char* p) {
 }
 __device__ inline void lds_store16(lds_char* p, const uint4& x) {
   *reinterpret_cast<lds_v4*>(p) = u32x4_t{x.x, x.y, x.z, x.w};
+}
+
+// An admitted row's 16-byte chunk to the state buffers.
+template <typename GG>
+__device__ __forceinline__ void store_row(char* p, const uint4& v) {
+  if constexpr (GG::kNtRows)
+    store16_nt(p, v);
+  else
+    store16(p, v);
 }
 
 // The unit's K and V rows (and E4M3 row scales) held in LDS by the resident
@@ -549,8 +562,8 @@ __device__ inline void admit_quantized(const UnitPtrs<GG>& u, int slot, const Re
     if (tid < LPR) {
       const uint4 kc = st->tokq[0][tid];
       const uint4 vc = st->tokq[1][tid];
-      store16(u.K + (size_t)slot * ROWB + tid * 16, kc);
-      store16(u.V + (size_t)slot * ROWB + tid * 16, vc);
+      store_row<GG>(u.K + (size_t)slot * ROWB + tid * 16, kc);
+      store_row<GG>(u.V + (size_t)slot * ROWB + tid * 16, vc);
       if constexpr (RES) {
         lds_store16(res->K + slot * ROWB + tid * 16, kc);
         lds_store16(res->V + slot * ROWB + tid * 16, vc);
@@ -574,7 +587,7 @@ __device__ inline void admit_quantized(const UnitPtrs<GG>& u, int slot, const Re
     load_input<GG>(is_v ? u.vn : u.kn, act ? c : 0, x);
     float sc;
     const uint4 codes = quantize_chunk<GG>(x, act, sc);
-    if (act) store16((is_v ? u.V : u.K) + (size_t)slot * ROWB + c * 16, codes);
+    if (act) store_row<GG>((is_v ? u.V : u.K) + (size_t)slot * ROWB + c * 16, codes);
     if (c == 0) (is_v ? u.vs : u.ks)[slot] = sc;
     if constexpr (RES) {
       if (act) lds_store16((is_v ? res->V : res->K) + slot * ROWB + c * 16, codes);
@@ -787,8 +800,8 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
     if (tid < LPR && dst >= 0) {
       const uint4 rk = lds_load16(res->K + v.ring_slot * ROWB + tid * 16);
       const uint4 rv = lds_load16(res->V + v.ring_slot * ROWB + tid * 16);
-      store16(u.K + (size_t)dst * ROWB + tid * 16, rk);
-      store16(u.V + (size_t)dst * ROWB + tid * 16, rv);
+      store_row<GG>(u.K + (size_t)dst * ROWB + tid * 16, rk);
+      store_row<GG>(u.V + (size_t)dst * ROWB + tid * 16, rv);
       lds_store16(res->K + dst * ROWB + tid * 16, rk);
       lds_store16(res->V + dst * ROWB + tid * 16, rv);
     }
@@ -798,23 +811,23 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
       } else if (tid < LPR) {
         const uint4 tk = lds_load16(res->K + v.k * ROWB + tid * 16);
         const uint4 tv = lds_load16(res->V + v.k * ROWB + tid * 16);
-        store16(u.K + (size_t)adm * ROWB + tid * 16, tk);
-        store16(u.V + (size_t)adm * ROWB + tid * 16, tv);
+        store_row<GG>(u.K + (size_t)adm * ROWB + tid * 16, tk);
+        store_row<GG>(u.V + (size_t)adm * ROWB + tid * 16, tv);
         lds_store16(res->K + adm * ROWB + tid * 16, tk);
         lds_store16(res->V + adm * ROWB + tid * 16, tv);
       }
     }
   } else {
     if (tid < LPR && dst >= 0) {
-      store16(u.K + (size_t)dst * ROWB + tid * 16, st->ring[0][tid]);
-      store16(u.V + (size_t)dst * ROWB + tid * 16, st->ring[1][tid]);
+      store_row<GG>(u.K + (size_t)dst * ROWB + tid * 16, st->ring[0][tid]);
+      store_row<GG>(u.V + (size_t)dst * ROWB + tid * 16, st->ring[1][tid]);
     }
     if (adm >= 0) {
       if constexpr (GG::kQuant) {
         admit_quantized<GG, false, TOK_STASHED>(u, adm, nullptr, st);
       } else if (tid < LPR) {
-        store16(u.K + (size_t)adm * ROWB + tid * 16, st->self[0][tid]);
-        store16(u.V + (size_t)adm * ROWB + tid * 16, st->self[1][tid]);
+        store_row<GG>(u.K + (size_t)adm * ROWB + tid * 16, st->self[0][tid]);
+        store_row<GG>(u.V + (size_t)adm * ROWB + tid * 16, st->self[1][tid]);
       }
     }
   }
@@ -906,11 +919,19 @@ __device__ __forceinline__ void unit_step(const DecodeArgs& a, int unit, StepSha
 
   const GroupMerge<NG> gm = merge_groups<GG, D>(m, lsum, o, sh.s_o, sh.s_m, sh.s_l);
   const float invL = 1.f / gm.L;
+  // The persistent launches at large batch store the output with the
+  // non-temporal hint: there one unit's stores go out while other units
+  // stream their rows, and the hint made those steps 3-5% faster; with one
+  // launch per step, or at small batch, it made them slower.
+  constexpr bool kNtOut = SL && !RES && NT <= 256;
   for (int c = tid; c < D; c += NT) {
     float acc = 0.f;
 #pragma unroll
     for (int g = 0; g < NG; ++g) acc = fmaf(sh.s_o[g][c], gm.wg[g], acc);
-    a.out[(size_t)unit * D + c] = acc * invL;
+    if constexpr (kNtOut)
+      __builtin_nontemporal_store(acc * invL, a.out + (size_t)unit * D + c);
+    else
+      a.out[(size_t)unit * D + c] = acc * invL;
   }
   finish_step<GG, RES, true, SL>(v, u, gm.M, invL, s_logit, sc_pf, ps_pf, &sh.st, sh.s_key, sh.s_slot, a.evicted,
                                  unit, res, in);
