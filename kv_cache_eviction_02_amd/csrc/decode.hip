@@ -673,14 +673,17 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
   };
   if constexpr (SL) {
     // Scores and positions in LDS (multi-step kernels), read per live slot:
-    // there the tail of one unit overlaps the streaming of others.
+    // there the tail of one unit overlaps the streaming of others.  Rounds
+    // past the live slots are skipped by a uniform test.
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
+      if (i * NT >= v.n_live) break;  // uniform
       const int j = tid + i * NT;
       ns_pf[i] = j < v.n_live ? s_logit[j] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
+      if (i * NT >= v.n_live) break;  // uniform
       const int j = tid + i * NT;
       if (j < v.n_live) {
         const int s = v.slot_of(j);
@@ -764,6 +767,7 @@ __device__ __forceinline__ void finish_step(const StepView& v, const UnitPtrs<GG
   };
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
+    if (i * NT >= v.n_live) break;  // uniform
     const int j = tid + i * NT;
     if (j < v.n_live) write_score(j, ns_pf[i]);
   }
