@@ -50,7 +50,7 @@ def alg_bytes_per_step(wl, cache="input"):
             + U * (2 * d * e + 8) + U * 4)
 
 
-PREFILL_CALLS = 7  # warm prefills timed one by one; the median is reported
+PREFILL_CALLS = 7  # warm prefills timed back to back; the mean per call is reported
 
 
 def prefill_flops(wl):
@@ -302,22 +302,22 @@ def run_gpu(wl, steps, warmup, waves, copy_mib=0, single_calls=False, split=0, c
     # one by one and the median is reported (one call varies with the clock).
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def median_prefill_ms(**kw):
+    # Back to back, like the decode steps and torch's attention below: the host's
+    # enqueueing of one call overlaps the GPU's work on the one before.
+    def mean_prefill_ms(**kw):
         cache.prefill(*prompt, **kw)
         torch.cuda.synchronize()
-        times = []
+        p0.record(stream)
         for _ in range(PREFILL_CALLS):
-            p0.record(stream)
             cache.prefill(*prompt, **kw)
-            p1.record(stream)
-            torch.cuda.synchronize()
-            times.append(p0.elapsed_time(p1))
-        return sorted(times)[len(times) // 2]
+        p1.record(stream)
+        torch.cuda.synchronize()
+        return p0.elapsed_time(p1) / PREFILL_CALLS
 
-    prefill_ms = median_prefill_ms()
+    prefill_ms = mean_prefill_ms()
     # The prefill that also returns the prompt's attention output.
     prompt_out = torch.empty((wl.batch, wl.heads, wl.prompt, wl.head_dim), dtype=torch.float32, device=dev)
-    prefill_out_ms = median_prefill_ms(out=prompt_out)
+    prefill_out_ms = mean_prefill_ms(out=prompt_out)
     del prompt_out
     # torch's own causal flash attention over the same prompt, for context (not in
     # counter runs, whose only copies calibrate the byte counters)
@@ -534,7 +534,7 @@ def main():
         },
         "prefill": {
             "ms": g["prefill_ms"],
-            "timing": f"median of {PREFILL_CALLS} warm calls",
+            "timing": f"mean of {PREFILL_CALLS} warm calls, back to back",
             "qk_tflops": prefill_flops(wl) / (g["prefill_ms"] * 1e-3) / 1e12,
             "peak_tflops": PEAK_BF16_TFLOPS if wl.kv_dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS,
             "frac": prefill_flops(wl) / (g["prefill_ms"] * 1e-3) / 1e12 /
