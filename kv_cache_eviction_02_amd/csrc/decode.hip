@@ -15,7 +15,7 @@
 // replaces each score by the current weight instead of adding it, and r = 0
 // (heavy-only) makes the decoded token itself a candidate.
 //
-// Three kernels share the streaming loop and the final score/eviction code:
+// Four kernels share the streaming loop and the final score/eviction code:
 //
 // decode_kernel: one workgroup per (batch, head) unit.  K and V rows are
 //   streamed once with 16-byte non-temporal loads, a row spread over
@@ -42,10 +42,18 @@
 //   workgroup carries its unit from step to step with the scores and positions
 //   in LDS, so one unit's end-of-step work overlaps the others' streaming.
 //
+// decode_resident_kernel: the same with the unit's K and V rows held in LDS
+//   for the whole launch (a long stream at small batch): a step reads only its
+//   inputs from memory, and the admission writes both copies.
+//
+// At large batch (up to four wavefronts per unit) the admitted rows are stored
+// with the non-temporal hint.
+//
 // E4M3 cache (C = e4m3, bf16 inputs): slots hold E4M3 codes with one float32
 // scale per row; the K scale multiplies the row's logit and the V scale its
-// weight.  The decoded token attends with its exact bf16 row and is quantized
-// on admission: codes of x * (448 / amax), scale amax / 448.
+// weight.  The decoded token attends with its exact bf16 row; its codes,
+// x * (448 / amax), and scale, amax / 448, are computed while the stream's
+// first rows are in flight and stored on admission.
 #include <float.h>
 #include <math.h>
 
