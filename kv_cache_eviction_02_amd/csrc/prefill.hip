@@ -18,8 +18,10 @@
 //              each wavefront owns 32 columns and walks the query rows in a
 //              fixed order, so the sums are deterministic without atomics;
 //   select   : per unit, radix select of the h largest c_j among the older
-//              positions, then the gather of the kept K/V rows into slots
-//              (quantized to E4M3 with per-row scales for an E4M3 cache).
+//              positions, then the gather of the heavy K/V rows into slots
+//              (quantized to E4M3 with per-row scales for an E4M3 cache); the
+//              window's rows, which no score decides, are copied by rowstats
+//              (or attend) while it runs.
 // The moving operand of both sweeps goes through LDS in chunks of 32 rows
 // shared by a block's four wavefronts, staged through registers one stage
 // ahead.  In each stage a wavefront reads the next chunk's fragments from LDS,
@@ -123,6 +125,146 @@ constexpr int kFixed = sizeof(T) == 2 ? 4 : 2;
 template <typename T>
 constexpr int rows_per_wave() { return kFixed<T> * kTile; }
 
+constexpr int ceil_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Cooperative copy of prompt rows into cache slots.  Unquantized caches move
+// 16-byte chunks; an E4M3 cache gives each row an aligned group of lanes,
+// 16 values per lane, which agree on the row maximum and write the codes of
+// x * (448 / amax) and the row scale amax / 448.
+template <typename T, typename C, int D>
+struct RowCopy {
+  static constexpr bool kQuant = std::is_same<C, e4m3>::value;
+  static constexpr int IROWB = D * Elem<T>::kBytes;   // prompt row bytes
+  static constexpr int CROWB = D * Elem<C>::kBytes;   // slot row bytes
+  static constexpr int ITEMS = kQuant ? D / 16 : IROWB / 16;  // work items per row
+  static constexpr int GW = kQuant ? ceil_pow2(ITEMS) : ITEMS;  // loop slots per row
+
+  // item c (0 <= c < GW) of prompt row p -> slot sl
+  __device__ static inline void item(const PrefillArgs& a, int unit, int P, int k, int p, int sl, int c) {
+    const char* Kp = (const char*)a.pk + ((size_t)unit * P + p) * IROWB;
+    const char* Vp = (const char*)a.pv + ((size_t)unit * P + p) * IROWB;
+    char* Ks = (char*)a.k_slots + ((size_t)unit * k + sl) * CROWB;
+    char* Vs = (char*)a.v_slots + ((size_t)unit * k + sl) * CROWB;
+    if constexpr (!kQuant) {
+      store16(Ks + c * 16, load16(Kp + c * 16));
+      store16(Vs + c * 16, load16(Vp + c * 16));
+    } else {
+      const bool act = c < ITEMS;
+      const int cc = act ? c : 0;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const char* src = w ? Vp : Kp;
+        float x[16];
+        Elem<T>::unpack(load16(src + cc * 32), x);
+        Elem<T>::unpack(load16(src + cc * 32 + 16), x + 8);
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+        amax = group_max<GW>(act ? amax : 0.f);
+        if (act) store16((w ? Vs : Ks) + c * 16, quantize16_e4m3(x, amax));
+        if (c == 0) (w ? a.v_scale : a.k_scale)[(size_t)unit * k + sl] = __fdiv_rn(amax, 448.f);
+      }
+    }
+  }
+};
+
+// The protected window, the newest n_ring = min(P, r) prompt positions (slot
+// p % r), is kept whatever the scores are (H2O summary, "The mechanism": the
+// recent window beside the heavy hitters).  The sweep over query rows (row
+// statistics, or the prompt output) therefore copies its rows into their slots
+// while it runs, a phase that leaves the memory system mostly idle, and the
+// selection afterwards copies only the heavy rows.  A unit's nblk blocks split
+// the window's rows evenly.  Unquantized rows: each thread loads its first
+// batch before the sweep's prologue, so the latency hides under the prologue's
+// own loads, and stores it after the prologue's first barrier; the rest of a
+// larger share, and an E4M3 window (quantized one aligned lane group per row),
+// are copied after the sweep.
+template <typename T, typename C, int D>
+struct WindowCopy {
+  using RC = RowCopy<T, C, D>;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kBatch = 2;  // items per thread in the first batch
+  int first, r, i0, i1;             // window rows start at position `first`; items [i0, i1), item = row * GW + c
+  uint4 kx[kBatch], vx[kBatch];
+
+  __device__ inline WindowCopy(const PrefillArgs& a, int blk, int nblk) {
+    const int n_ring = min(a.P, a.r);
+    first = a.P - n_ring;
+    r = a.r;
+    i0 = (int)((long long)n_ring * blk / nblk) * RC::GW;
+    i1 = (int)((long long)n_ring * (blk + 1) / nblk) * RC::GW;
+  }
+  __device__ inline int pos_of(int i) const { return first + i / RC::GW; }
+  __device__ inline size_t src_off(int unit, int P, int i) const {
+    return ((size_t)unit * P + pos_of(i)) * RC::IROWB + (i % RC::GW) * 16;
+  }
+  __device__ inline size_t dst_off(int unit, int k, int i) const {
+    return ((size_t)unit * k + pos_of(i) % r) * RC::CROWB + (i % RC::GW) * 16;
+  }
+  // Unquantized: loads of the first batch (addresses clamped into the share).
+  __device__ inline void load_first(const PrefillArgs& a, int unit) {
+    if constexpr (!RC::kQuant) {
+      if (i1 > i0) {  // uniform
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const size_t off = src_off(unit, a.P, min(i0 + (int)threadIdx.x + u * kThreads, i1 - 1));
+          kx[u] = load16((const char*)a.pk + off);
+          vx[u] = load16((const char*)a.pv + off);
+        }
+      }
+    }
+  }
+  // Unquantized: stores of the first batch.
+  __device__ inline void store_first(const PrefillArgs& a, int unit) {
+    if constexpr (!RC::kQuant) {
+      if (i1 <= i0) return;  // uniform
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int i = i0 + (int)threadIdx.x + u * kThreads;
+        if (i < i1) {
+          const size_t off = dst_off(unit, a.k, i);
+          store16((char*)a.k_slots + off, kx[u]);
+          store16((char*)a.v_slots + off, vx[u]);
+        }
+      }
+    }
+  }
+  // The rest of the share (unquantized), or all of it quantized to E4M3 codes
+  // and per-row scales.  Called by every thread of the block.
+  __device__ inline void rest(const PrefillArgs& a, int unit) {
+    const int tid = threadIdx.x;
+    if constexpr (!RC::kQuant) {
+      for (int base = i0 + kBatch * kThreads; base < i1; base += kBatch * kThreads) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const size_t off = src_off(unit, a.P, min(base + tid + u * kThreads, i1 - 1));
+          kx[u] = load16((const char*)a.pk + off);
+          vx[u] = load16((const char*)a.pv + off);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int i = base + tid + u * kThreads;
+          if (i < i1) {
+            const size_t off = dst_off(unit, a.k, i);
+            store16((char*)a.k_slots + off, kx[u]);
+            store16((char*)a.v_slots + off, vx[u]);
+          }
+        }
+      }
+    } else {
+      // i0 and i1 are whole rows and GW divides the block, so a row's lane group is in or out together
+      for (int base = i0; base < i1; base += kThreads) {
+        const int i = base + tid;
+        if (i < i1) RC::item(a, unit, a.P, a.k, pos_of(i), pos_of(i) % r, i % RC::GW);
+      }
+    }
+  }
+};
+
 // ---- prompt attention output --------------------------------------------------
 //
 // O_i = sum_{j <= i} softmax_i(s_ij) v_j for every prompt row (the full causal
@@ -178,7 +320,7 @@ __device__ inline void load_lds_frag(Frag<T, D>& f, const char* base, int row0, 
   for (int i = 0; i < Frag<T, D>::kChunks; ++i) f.c[i] = *reinterpret_cast<const uint4*>(p + 64 * i);
 }
 
-template <typename T, int D>
+template <typename T, typename C, int D>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void attend_kernel(
     PrefillArgs a, int stride, int nblk) {
   using AT = AttendTile<T, D>;
@@ -204,6 +346,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const char* Vb = (const char*)a.pv + (size_t)unit * P * AT::ROWB;
   const float sc = a.scale_log2;
 
+  WindowCopy<T, C, D> win(a, blk, nblk);
+  win.load_first(a, unit);
   Frag<T, D> fq[QS];
 #pragma unroll
   for (int q = 0; q < QS; ++q) fq[q].load(Qb, qw0 + q * kTile, P, lane);
@@ -345,6 +489,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   fetch(0);
   stash(0, 0);
   __syncthreads();
+  win.store_first(a, unit);
   for (int ch = 0; ch < nch; ++ch) {
     if (ch + 1 < nch) fetch(ch + 1);
     const char* kl = smem + (ch % AT::NBUF) * AT::BUF;
@@ -353,6 +498,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     if (ch + 1 < nch) stash(ch + 1, (ch + 1) % AT::NBUF);
     __syncthreads();
   }
+  win.rest(a, unit);
 
   if (qw0 >= P) return;
 #pragma unroll
@@ -408,7 +554,7 @@ struct RowTile {
   static constexpr int BUF = KC * KSTR;
 };
 
-template <typename T, int D>
+template <typename T, typename C, int D>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void rowstats_kernel(
     PrefillArgs a, int stride, int nblk) {
   using RT = RowTile<T, D>;
@@ -432,6 +578,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const char* Kb = (const char*)a.pk + (size_t)unit * P * RT::ROWB;
   const float sc = pin_arg(a.scale_log2);
 
+  WindowCopy<T, C, D> win(a, blk, nblk);
+  win.load_first(a, unit);
   Frag<T, D> fq[QS];
 #pragma unroll
   for (int q = 0; q < QS; ++q) fq[q].load_clamped(Qb, qw0 + q * kTile, P, lane);  // rows past P: not written
@@ -571,6 +719,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     stash(1);
   }
   __syncthreads();
+  win.store_first(a, unit);
   if (active(0)) {
     Frag<T, D> fk[2];
     read(0, fk);
@@ -578,6 +727,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   }
   __syncthreads();  // every wavefront has read chunk 0 before chunk 2 replaces it
   for (int ch = 0; ch < nch; ++ch) stage(ch, s);
+  win.rest(a, unit);
 
   if (qw0 >= P) return;
 #pragma unroll
@@ -827,53 +977,6 @@ __device__ inline int block_exclusive_scan(int v, int* buf, int* total) {
   return incl - v;
 }
 
-constexpr int ceil_pow2(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
-}
-
-// Cooperative copy of prompt rows into cache slots.  Unquantized caches move
-// 16-byte chunks; an E4M3 cache gives each row an aligned group of lanes,
-// 16 values per lane, which agree on the row maximum and write the codes of
-// x * (448 / amax) and the row scale amax / 448.
-template <typename T, typename C, int D>
-struct RowCopy {
-  static constexpr bool kQuant = std::is_same<C, e4m3>::value;
-  static constexpr int IROWB = D * Elem<T>::kBytes;   // prompt row bytes
-  static constexpr int CROWB = D * Elem<C>::kBytes;   // slot row bytes
-  static constexpr int ITEMS = kQuant ? D / 16 : IROWB / 16;  // work items per row
-  static constexpr int GW = kQuant ? ceil_pow2(ITEMS) : ITEMS;  // loop slots per row
-
-  // item c (0 <= c < GW) of prompt row p -> slot sl
-  __device__ static inline void item(const PrefillArgs& a, int unit, int P, int k, int p, int sl, int c) {
-    const char* Kp = (const char*)a.pk + ((size_t)unit * P + p) * IROWB;
-    const char* Vp = (const char*)a.pv + ((size_t)unit * P + p) * IROWB;
-    char* Ks = (char*)a.k_slots + ((size_t)unit * k + sl) * CROWB;
-    char* Vs = (char*)a.v_slots + ((size_t)unit * k + sl) * CROWB;
-    if constexpr (!kQuant) {
-      store16(Ks + c * 16, load16(Kp + c * 16));
-      store16(Vs + c * 16, load16(Vp + c * 16));
-    } else {
-      const bool act = c < ITEMS;
-      const int cc = act ? c : 0;
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const char* src = w ? Vp : Kp;
-        float x[16];
-        Elem<T>::unpack(load16(src + cc * 32), x);
-        Elem<T>::unpack(load16(src + cc * 32 + 16), x + 8);
-        float amax = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
-        amax = group_max<GW>(act ? amax : 0.f);
-        if (act) store16((w ? Vs : Ks) + c * 16, quantize16_e4m3(x, amax));
-        if (c == 0) (w ? a.v_scale : a.k_scale)[(size_t)unit * k + sl] = __fdiv_rn(amax, 448.f);
-      }
-    }
-  }
-};
-
 template <typename T, typename C, int D>
 __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs a, int stride) {
   using RC = RowCopy<T, C, D>;
@@ -970,13 +1073,13 @@ __global__ __launch_bounds__(kSelThreads) void select_gather_kernel(PrefillArgs 
   }
   __syncthreads();  // the positions just written are read back below
 
-  // Row copies: the used slots in order (ring, then heavy), GW consecutive
-  // lanes per row, each slot's source position read back from pos.  For an
-  // unquantized cache every thread first issues the loads of up to kBatch
-  // items, then their stores, so many rows are in flight at once.
-  const int n_rows = n_ring + n_sel;
-  const int n_items = n_rows * GW;
-  auto slot_of_row = [&](int row) { return row < n_ring ? row : r + (row - n_ring); };
+  // Row copies of the heavy slots (the sweep over query rows has copied the
+  // window's), GW consecutive lanes per row, each slot's source position read
+  // back from pos.  For an unquantized cache every thread first issues the
+  // loads of up to kBatch items, then their stores, so many rows are in flight
+  // at once.
+  const int n_items = n_sel * GW;
+  auto slot_of_row = [&](int row) { return r + row; };
   if constexpr (!RC::kQuant) {
     constexpr int kBatch = 4;
     constexpr int IROWB = RC::IROWB;
@@ -1022,11 +1125,11 @@ hipError_t launch_prefill_td(const PrefillArgs& a, int stride, hipStream_t s) {
   if (a.out) {
     constexpr int bq = AttendTile<T, D>::BQ;
     const int nb = (a.P + bq - 1) / bq;
-    hipLaunchKernelGGL((attend_kernel<T, D>), dim3((unsigned)(nb * a.units)), block, 0, s, a, stride, nb);
+    hipLaunchKernelGGL((attend_kernel<T, C, D>), dim3((unsigned)(nb * a.units)), block, 0, s, a, stride, nb);
   } else {
     constexpr int bq = RowTile<T, D>::BQ;
     const int nb = (a.P + bq - 1) / bq;
-    hipLaunchKernelGGL((rowstats_kernel<T, D>), dim3((unsigned)(nb * a.units)), block, 0, s, a, stride, nb);
+    hipLaunchKernelGGL((rowstats_kernel<T, C, D>), dim3((unsigned)(nb * a.units)), block, 0, s, a, stride, nb);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
