@@ -177,12 +177,21 @@ struct RowCopy {
 // recent window beside the heavy hitters).  The sweep over query rows (row
 // statistics, or the prompt output) therefore copies its rows into their slots
 // while it runs, a phase that leaves the memory system mostly idle, and the
-// selection afterwards copies only the heavy rows.  A unit's nblk blocks split
-// the window's rows evenly.  Unquantized rows: each thread loads its first
-// batch before the sweep's prologue, so the latency hides under the prologue's
-// own loads, and stores it after the prologue's first barrier; the rest of a
-// larger share, and an E4M3 window (quantized one aligned lane group per row),
-// are copied after the sweep.
+// selection afterwards copies only the heavy rows.  The window's rows are split
+// evenly over `ncopy` of a unit's blocks (blk < ncopy).
+//
+// A block that copies pays about one memory latency for it: stores issued
+// mid-sweep make the next tile-load wait also wait for their acknowledgement
+// (vector-memory completions are counted in issue order), and a copy after the
+// sweep waits for its own loads.  The row statistics therefore give the
+// unquantized window to the two shortest blocks of each unit (blk 0 and 1),
+// which copy it after their sweep with 8 items per thread in flight: measured
+// at opt30b, the sweep then costs what it did without the copy, where copying
+// in all eight blocks cost it 5%.  The prompt-output sweep, whose stages are
+// about twice as long, absorbs a copy split over all its blocks: each thread
+// loads its first batch before the prologue and stores it after the
+// prologue's first barrier.  An E4M3 window is quantized one aligned lane
+// group per row, after the sweep, by all blocks.
 template <typename T, typename C, int D>
 struct WindowCopy {
   using RC = RowCopy<T, C, D>;
@@ -191,12 +200,13 @@ struct WindowCopy {
   int first, r, i0, i1;             // window rows start at position `first`; items [i0, i1), item = row * GW + c
   uint4 kx[kBatch], vx[kBatch];
 
-  __device__ inline WindowCopy(const PrefillArgs& a, int blk, int nblk) {
+  __device__ inline WindowCopy(const PrefillArgs& a, int blk, int nblk, int ncopy) {
     const int n_ring = min(a.P, a.r);
     first = a.P - n_ring;
     r = a.r;
-    i0 = (int)((long long)n_ring * blk / nblk) * RC::GW;
-    i1 = (int)((long long)n_ring * (blk + 1) / nblk) * RC::GW;
+    const int nb = min(ncopy, nblk);
+    i0 = blk < nb ? (int)((long long)n_ring * blk / nb) * RC::GW : 0;
+    i1 = blk < nb ? (int)((long long)n_ring * (blk + 1) / nb) * RC::GW : 0;
   }
   __device__ inline int pos_of(int i) const { return first + i / RC::GW; }
   __device__ inline size_t src_off(int unit, int P, int i) const {
@@ -233,25 +243,28 @@ struct WindowCopy {
       }
     }
   }
-  // The rest of the share (unquantized), or all of it quantized to E4M3 codes
-  // and per-row scales.  Called by every thread of the block.
-  __device__ inline void rest(const PrefillArgs& a, int unit) {
+  // Unquantized items [from, i1) of the share, RB per thread in flight; or the
+  // whole share quantized to E4M3 codes and per-row scales.  Called by every
+  // thread of the block.
+  template <int RB>
+  __device__ inline void copy(const PrefillArgs& a, int unit, int from) {
     const int tid = threadIdx.x;
     if constexpr (!RC::kQuant) {
-      for (int base = i0 + kBatch * kThreads; base < i1; base += kBatch * kThreads) {
+      for (int base = from; base < i1; base += RB * kThreads) {
+        uint4 kb[RB], vb[RB];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
+        for (int u = 0; u < RB; ++u) {
           const size_t off = src_off(unit, a.P, min(base + tid + u * kThreads, i1 - 1));
-          kx[u] = load16((const char*)a.pk + off);
-          vx[u] = load16((const char*)a.pv + off);
+          kb[u] = load16((const char*)a.pk + off);
+          vb[u] = load16((const char*)a.pv + off);
         }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
+        for (int u = 0; u < RB; ++u) {
           const int i = base + tid + u * kThreads;
           if (i < i1) {
             const size_t off = dst_off(unit, a.k, i);
-            store16((char*)a.k_slots + off, kx[u]);
-            store16((char*)a.v_slots + off, vx[u]);
+            store16((char*)a.k_slots + off, kb[u]);
+            store16((char*)a.v_slots + off, vb[u]);
           }
         }
       }
@@ -263,6 +276,10 @@ struct WindowCopy {
       }
     }
   }
+  // After load_first / store_first: the rest of the share.
+  __device__ inline void rest(const PrefillArgs& a, int unit) { copy<kBatch>(a, unit, i0 + kBatch * kThreads); }
+  // The whole share, after the sweep.
+  __device__ inline void all(const PrefillArgs& a, int unit) { copy<8>(a, unit, i0); }
 };
 
 // ---- prompt attention output --------------------------------------------------
@@ -346,7 +363,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const char* Vb = (const char*)a.pv + (size_t)unit * P * AT::ROWB;
   const float sc = a.scale_log2;
 
-  WindowCopy<T, C, D> win(a, blk, nblk);
+  WindowCopy<T, C, D> win(a, blk, nblk, nblk);
   win.load_first(a, unit);
   Frag<T, D> fq[QS];
 #pragma unroll
@@ -578,8 +595,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const char* Kb = (const char*)a.pk + (size_t)unit * P * RT::ROWB;
   const float sc = pin_arg(a.scale_log2);
 
-  WindowCopy<T, C, D> win(a, blk, nblk);
-  win.load_first(a, unit);
+  WindowCopy<T, C, D> win(a, blk, nblk, RowCopy<T, C, D>::kQuant ? nblk : 2);
   Frag<T, D> fq[QS];
 #pragma unroll
   for (int q = 0; q < QS; ++q) fq[q].load_clamped(Qb, qw0 + q * kTile, P, lane);  // rows past P: not written
@@ -719,7 +735,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     stash(1);
   }
   __syncthreads();
-  win.store_first(a, unit);
   if (active(0)) {
     Frag<T, D> fk[2];
     read(0, fk);
@@ -727,7 +742,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   }
   __syncthreads();  // every wavefront has read chunk 0 before chunk 2 replaces it
   for (int ch = 0; ch < nch; ++ch) stage(ch, s);
-  win.rest(a, unit);
+  win.all(a, unit);
 
   if (qw0 >= P) return;
 #pragma unroll
