@@ -115,6 +115,28 @@ __device__ inline int xcd_local_block(int total) {
   return (L % 8) * (total / 8) + L / 8;
 }
 
+// Sweep blocks: id = unit * nblk + j, where j = 0 is the unit's longest block,
+// so each XCD takes its units one after another, longest block first.  The
+// last kTailUnits units of each XCD's range are interleaved instead (all their
+// longest blocks, then all their second longest, ...): otherwise the final
+// unit's longest block starts last and runs alone at the end of the launch.
+constexpr int kTailUnits = 16;
+__device__ inline int sweep_block(int total, int nblk) {
+  int id = xcd_local_block(total);
+  const int n = total / 8;  // blocks per XCD
+  if (total % 8 == 0 && n % nblk == 0) {
+    const int x0 = id - id % n;
+    const int i = id - x0;
+    const int wu = min(kTailUnits, n / nblk);
+    const int w0 = n - wu * nblk;
+    if (i >= w0) {
+      const int k = i - w0;
+      id = x0 + w0 + (k % wu) * nblk + k / wu;
+    }
+  }
+  return id;
+}
+
 constexpr int kWaves = 4;  // wavefronts per block, each with its own rows
 
 // Fixed 16-row subtiles held by one wavefront (B operands): 64 rows for bf16,
@@ -346,7 +368,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   constexpr float kLow = -1.0e30f;
   __shared__ __attribute__((aligned(16))) char smem[AT::NBUF * AT::BUF];
 
-  const int id = xcd_local_block(nblk * a.units);
+  const int id = sweep_block(nblk * a.units, nblk);
   const int unit = id / nblk;
   const int blk = nblk - 1 - id % nblk;  // longest rows first
   const int tid = threadIdx.x;
@@ -579,7 +601,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   constexpr float kLow = -1.0e30f;
   __shared__ __attribute__((aligned(16))) char smem[2 * RT::BUF];
 
-  const int id = xcd_local_block(nblk * a.units);
+  const int id = sweep_block(nblk * a.units, nblk);
   const int unit = id / nblk;
   const int blk = nblk - 1 - id % nblk;  // longest rows first
   const int tid = threadIdx.x;
@@ -794,7 +816,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   constexpr int QS = CT::QS;
   __shared__ __attribute__((aligned(16))) char smem[2 * CT::BUF];
 
-  const int id = xcd_local_block(nblk * a.units);
+  const int id = sweep_block(nblk * a.units, nblk);
   const int unit = id / nblk;
   const int blk = id % nblk;  // first columns have the most rows
   const int tid = threadIdx.x;
