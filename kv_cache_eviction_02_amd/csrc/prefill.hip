@@ -637,27 +637,28 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     const int idx = min(tid + u * kWaves * 64, RT::PIECES - 1);
     thr_off[u] = (idx / (RT::ROWB / 16)) * RT::ROWB + (idx % (RT::ROWB / 16)) * 16;
   }
-  auto fetch = [&](int ch) __attribute__((always_inline)) {
+  // Chunks past the block's keys clamp their rows, so any ch is a valid fetch.
+  auto fetch = [&](int ch, uint4 (&r)[RT::PER_T]) __attribute__((always_inline)) {
     if ((ch + 1) * RT::KC <= kend) {  // uniform
       const char* cb = Kb + (size_t)ch * RT::KC * RT::ROWB;
 #pragma unroll
-      for (int u = 0; u < RT::PER_T; ++u) rk[u] = load16(cb + thr_off[u]);
+      for (int u = 0; u < RT::PER_T; ++u) r[u] = load16(cb + thr_off[u]);
     } else {
 #pragma unroll
       for (int u = 0; u < RT::PER_T; ++u) {
         const int idx = min(tid + u * kWaves * 64, RT::PIECES - 1);
         const int key = min(ch * RT::KC + idx / (RT::ROWB / 16), kend - 1);
-        rk[u] = load16(Kb + (size_t)key * RT::ROWB + (idx % (RT::ROWB / 16)) * 16);
+        r[u] = load16(Kb + (size_t)key * RT::ROWB + (idx % (RT::ROWB / 16)) * 16);
       }
     }
   };
-  auto stash = [&](int b) __attribute__((always_inline)) {
+  auto stash = [&](int b, const uint4 (&r)[RT::PER_T]) __attribute__((always_inline)) {
     char* kl = smem + b * RT::BUF;
 #pragma unroll
     for (int u = 0; u < RT::PER_T; ++u) {
       const int idx = tid + u * kWaves * 64;
       if (RT::PIECES % (kWaves * 64) == 0 || idx < RT::PIECES)  // no branch when the block covers the chunk evenly
-        *reinterpret_cast<uint4*>(kl + (idx / (RT::ROWB / 16)) * RT::KSTR + (idx % (RT::ROWB / 16)) * 16) = rk[u];
+        *reinterpret_cast<uint4*>(kl + (idx / (RT::ROWB / 16)) * RT::KSTR + (idx % (RT::ROWB / 16)) * 16) = r[u];
     }
   };
   // Keys past kend hold copies of row kend - 1: they follow every query of the
@@ -735,7 +736,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   auto stage = [&](int ch, f32x4 (&s)[2][QS]) __attribute__((always_inline)) {
     const bool diag = ch * RT::KC + RT::KC - 1 > qw0;
     const bool next = active(ch + 1);
-    if (ch + 2 < nch) fetch(ch + 2);
+    if (ch + 2 < nch) fetch(ch + 2, rk);
     Frag<T, D> fk[2];
     if (next) read(ch + 1, fk);
     if (active(ch)) {
@@ -745,16 +746,21 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
         soft(std::false_type{}, ch, s);
     }
     if (next) mult(fk, s);
-    if (ch + 2 < nch) stash(ch & 1);  // chunk ch + 2 replaces chunk ch, read one stage ago
+    if (ch + 2 < nch) stash(ch & 1, rk);  // chunk ch + 2 replaces chunk ch, read one stage ago
     __syncthreads();
   };
 
   f32x4 s[2][QS];
-  fetch(0);
-  stash(0);
-  if (nch > 1) {
-    fetch(1);
-    stash(1);
+  {
+    // Both first chunks' loads are in flight before the first wait for either.
+    // Buffer 1 is written even for a single chunk (it is then never read): a
+    // conditional store would let the compiler sink chunk 1's loads behind the
+    // wait for chunk 0.
+    uint4 rk1[RT::PER_T];
+    fetch(0, rk);
+    fetch(1, rk1);
+    stash(0, rk);
+    stash(1, rk1);
   }
   __syncthreads();
   if (active(0)) {
@@ -853,33 +859,34 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     const int idx = min(tid + u * kWaves * 64, CT::PIECES - 1);
     thr_off[u] = (idx / (CT::ROWB / 16)) * CT::ROWB + (idx % (CT::ROWB / 16)) * 16;
   }
-  auto fetch = [&](int ch) __attribute__((always_inline)) {
+  // Chunks past the prompt clamp their rows, so any ch is a valid fetch.
+  auto fetch = [&](int ch, uint4 (&r)[CT::PER_T], float& l) __attribute__((always_inline)) {
     if ((ch + 1) * CT::QC <= P) {  // uniform
       const char* cb = Qb + (size_t)ch * CT::QC * CT::ROWB;
 #pragma unroll
-      for (int u = 0; u < CT::PER_T; ++u) rq[u] = load16(cb + thr_off[u]);
-      if (tid < CT::QC) rl = lse[ch * CT::QC + tid];
+      for (int u = 0; u < CT::PER_T; ++u) r[u] = load16(cb + thr_off[u]);
+      if (tid < CT::QC) l = lse[ch * CT::QC + tid];
     } else {
 #pragma unroll
       for (int u = 0; u < CT::PER_T; ++u) {
         const int idx = min(tid + u * kWaves * 64, CT::PIECES - 1);
         const int row = min(ch * CT::QC + idx / (CT::ROWB / 16), P - 1);
-        rq[u] = load16(Qb + (size_t)row * CT::ROWB + (idx % (CT::ROWB / 16)) * 16);
+        r[u] = load16(Qb + (size_t)row * CT::ROWB + (idx % (CT::ROWB / 16)) * 16);
       }
-      if (tid < CT::QC) rl = lse[min(ch * CT::QC + tid, P - 1)];
+      if (tid < CT::QC) l = lse[min(ch * CT::QC + tid, P - 1)];
     }
   };
   // Chunk c's rows and lse values go to buffer (c - ch0) & 1.
-  auto stash = [&](int b) __attribute__((always_inline)) {
+  auto stash = [&](int b, const uint4 (&r)[CT::PER_T], float l) __attribute__((always_inline)) {
     char* ql = smem + b * CT::BUF;
 #pragma unroll
     for (int u = 0; u < CT::PER_T; ++u) {
       const int idx = tid + u * kWaves * 64;
       if (CT::PIECES % (kWaves * 64) == 0 || idx < CT::PIECES)  // no branch when the block covers the chunk evenly
         *reinterpret_cast<uint4*>(ql + (idx / (CT::ROWB / 16)) * CT::QSTR + (idx % (CT::ROWB / 16)) * 16) =
-            rq[u];
+            r[u];
     }
-    if (tid < CT::QC) reinterpret_cast<float*>(ql + CT::QC * CT::QSTR)[tid] = rl;
+    if (tid < CT::QC) reinterpret_cast<float*>(ql + CT::QC * CT::QSTR)[tid] = l;
   };
   // A chunk's query fragments and lse values, into registers (the buffer is
   // refilled one stage later), then its S tiles (acc[i]: query 4g + i of the
@@ -951,7 +958,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   auto stage = [&](int ch, f32x4 (&s)[2][QS], float4 (&lq)[2]) __attribute__((always_inline)) {
     const int c0 = ch * CT::QC;
     const bool cur = active(ch), next = active(ch + 1);
-    if (ch + 2 < nch) fetch(ch + 2);
+    if (ch + 2 < nch) fetch(ch + 2, rq, rl);
     Frag<T, D> fq[2];
     read(ch + 1, fq);
     if (cur) {
@@ -964,17 +971,21 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     }
     if (next) mult(fq, s);
     read_lse(ch + 1, lq);
-    if (ch + 2 < nch) stash((ch - ch0) & 1);  // chunk ch + 2 replaces chunk ch, read one stage ago
+    if (ch + 2 < nch) stash((ch - ch0) & 1, rq, rl);  // chunk ch + 2 replaces chunk ch, read one stage ago
     __syncthreads();
   };
 
   f32x4 s[2][QS];
   float4 lq[2];
-  fetch(ch0);
-  stash(0);
-  if (ch0 + 1 < nch) {
-    fetch(ch0 + 1);
-    stash(1);
+  {
+    // Both first chunks' loads are in flight before the first wait for either
+    // (buffer 1 is written even when it is never read, as in the row statistics).
+    uint4 rq1[CT::PER_T];
+    float rl1 = 0.f;
+    fetch(ch0, rq, rl);
+    fetch(ch0 + 1, rq1, rl1);
+    stash(0, rq, rl);
+    stash(1, rq1, rl1);
   }
   __syncthreads();
   if (active(ch0)) {
