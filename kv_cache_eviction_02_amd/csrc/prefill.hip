@@ -165,31 +165,48 @@ struct RowCopy {
   static constexpr int ITEMS = kQuant ? D / 16 : IROWB / 16;  // work items per row
   static constexpr int GW = kQuant ? ceil_pow2(ITEMS) : ITEMS;  // loop slots per row
 
+  // E4M3: item c of prompt row p, loaded (K's 16 values, then V's).
+  __device__ static inline void load_q(const PrefillArgs& a, int unit, int P, int p, int c, uint4 (&x)[4]) {
+    const int cc = c < ITEMS ? c : 0;
+    const char* Kp = (const char*)a.pk + ((size_t)unit * P + p) * IROWB + cc * 32;
+    const char* Vp = (const char*)a.pv + ((size_t)unit * P + p) * IROWB + cc * 32;
+    x[0] = load16(Kp);
+    x[1] = load16(Kp + 16);
+    x[2] = load16(Vp);
+    x[3] = load16(Vp + 16);
+  }
+  // E4M3: the codes and row scales of a loaded item, into slot sl.  Every lane
+  // of the row's group takes part (the row maximum is a group reduction).
+  __device__ static inline void store_q(const PrefillArgs& a, int unit, int k, int sl, int c, const uint4 (&x)[4]) {
+    const bool act = c < ITEMS;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      float v[16];
+      Elem<T>::unpack(x[2 * w], v);
+      Elem<T>::unpack(x[2 * w + 1], v + 8);
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+      amax = group_max<GW>(act ? amax : 0.f);
+      char* dst = (char*)(w ? a.v_slots : a.k_slots) + ((size_t)unit * k + sl) * CROWB;
+      if (act) store16(dst + c * 16, quantize16_e4m3(v, amax));
+      if (c == 0) (w ? a.v_scale : a.k_scale)[(size_t)unit * k + sl] = __fdiv_rn(amax, 448.f);
+    }
+  }
+
   // item c (0 <= c < GW) of prompt row p -> slot sl
   __device__ static inline void item(const PrefillArgs& a, int unit, int P, int k, int p, int sl, int c) {
-    const char* Kp = (const char*)a.pk + ((size_t)unit * P + p) * IROWB;
-    const char* Vp = (const char*)a.pv + ((size_t)unit * P + p) * IROWB;
-    char* Ks = (char*)a.k_slots + ((size_t)unit * k + sl) * CROWB;
-    char* Vs = (char*)a.v_slots + ((size_t)unit * k + sl) * CROWB;
     if constexpr (!kQuant) {
+      const char* Kp = (const char*)a.pk + ((size_t)unit * P + p) * IROWB;
+      const char* Vp = (const char*)a.pv + ((size_t)unit * P + p) * IROWB;
+      char* Ks = (char*)a.k_slots + ((size_t)unit * k + sl) * CROWB;
+      char* Vs = (char*)a.v_slots + ((size_t)unit * k + sl) * CROWB;
       store16(Ks + c * 16, load16(Kp + c * 16));
       store16(Vs + c * 16, load16(Vp + c * 16));
     } else {
-      const bool act = c < ITEMS;
-      const int cc = act ? c : 0;
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const char* src = w ? Vp : Kp;
-        float x[16];
-        Elem<T>::unpack(load16(src + cc * 32), x);
-        Elem<T>::unpack(load16(src + cc * 32 + 16), x + 8);
-        float amax = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
-        amax = group_max<GW>(act ? amax : 0.f);
-        if (act) store16((w ? Vs : Ks) + c * 16, quantize16_e4m3(x, amax));
-        if (c == 0) (w ? a.v_scale : a.k_scale)[(size_t)unit * k + sl] = __fdiv_rn(amax, 448.f);
-      }
+      uint4 x[4];
+      load_q(a, unit, P, p, c, x);
+      store_q(a, unit, k, sl, c, x);
     }
   }
 };
@@ -206,14 +223,14 @@ struct RowCopy {
 // mid-sweep make the next tile-load wait also wait for their acknowledgement
 // (vector-memory completions are counted in issue order), and a copy after the
 // sweep waits for its own loads.  The row statistics therefore give the
-// unquantized window to the two shortest blocks of each unit (blk 0 and 1),
-// which copy it after their sweep with 8 items per thread in flight: measured
-// at opt30b, the sweep then costs what it did without the copy, where copying
-// in all eight blocks cost it 5%.  The prompt-output sweep, whose stages are
+// window to the two shortest blocks of each unit (blk 0 and 1), which copy it
+// after their sweep with 8 items (E4M3: 4, at d = 64 2) per thread in flight: measured at
+// opt30b, the sweep then costs what it did without the copy, where copying in
+// all eight blocks cost it 5%.  The prompt-output sweep, whose stages are
 // about twice as long, absorbs a copy split over all its blocks: each thread
 // loads its first batch before the prologue and stores it after the
-// prologue's first barrier.  An E4M3 window is quantized one aligned lane
-// group per row, after the sweep, by all blocks.
+// prologue's first barrier (E4M3: after the sweep).  E4M3 rows are quantized
+// one aligned lane group per row.
 template <typename T, typename C, int D>
 struct WindowCopy {
   using RC = RowCopy<T, C, D>;
@@ -291,10 +308,22 @@ struct WindowCopy {
         }
       }
     } else {
-      // i0 and i1 are whole rows and GW divides the block, so a row's lane group is in or out together
-      for (int base = i0; base < i1; base += kThreads) {
-        const int i = base + tid;
-        if (i < i1) RC::item(a, unit, a.P, a.k, pos_of(i), pos_of(i) % r, i % RC::GW);
+      // i0 and i1 are whole rows and GW divides the block, so a row's lane
+      // group is in or out together.  The loads of RB items per thread are
+      // issued before any of them is quantized.
+      constexpr int QB = RB < 4 ? RB : (D >= 96 ? 4 : 2);  // d = 64: 2 keeps the sweep's occupancy
+      for (int base = i0; base < i1; base += QB * kThreads) {
+        uint4 x[QB][4];
+#pragma unroll
+        for (int u = 0; u < QB; ++u) {
+          const int i = min(base + tid + u * kThreads, i1 - 1);
+          RC::load_q(a, unit, a.P, pos_of(i), i % RC::GW, x[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < QB; ++u) {
+          const int i = base + tid + u * kThreads;
+          if (i < i1) RC::store_q(a, unit, a.k, pos_of(i) % r, i % RC::GW, x[u]);
+        }
       }
     }
   }
@@ -617,7 +646,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const char* Kb = (const char*)a.pk + (size_t)unit * P * RT::ROWB;
   const float sc = pin_arg(a.scale_log2);
 
-  WindowCopy<T, C, D> win(a, blk, nblk, RowCopy<T, C, D>::kQuant ? nblk : 2);
+  WindowCopy<T, C, D> win(a, blk, nblk, 2);
   Frag<T, D> fq[QS];
 #pragma unroll
   for (int q = 0; q < QS; ++q) fq[q].load_clamped(Qb, qw0 + q * kTile, P, lane);  // rows past P: not written
