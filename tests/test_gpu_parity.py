@@ -742,6 +742,33 @@ def test_prompt_output_large_prompt_and_e4m3_cache():
     run_workload(wl, 2, 8, kv_every=4, prompt_output=True, cache="e4m3")
 
 
+# ---- the window's rows, copied by the sweep over query rows --------------------------
+
+WINDOW = [
+    # one window row: most of the unit's blocks have no share of it
+    Workload(120, "window_one_row_bf16_d128", 1, 2, 128, 300, 4, 1, 20, "bf16", "fraction", skew_frac=0.1),
+    # window wider than the prompt: every prompt row is a window row, several copy batches per block
+    Workload(121, "window_whole_prompt_bf16_d128", 1, 2, 128, 200, 4, 256, 16, "bf16", "fraction",
+             skew_frac=0.1),
+    # d = 64 (E4M3 rows copied two per thread at a time) with many window rows per block
+    Workload(122, "window_wide_bf16_d64", 1, 2, 64, 700, 4, 600, 40, "bf16", "fraction", skew_frac=0.1),
+    # shares that do not divide evenly, d = 96
+    Workload(123, "window_ragged_bf16_d96", 1, 2, 96, 1000, 4, 333, 100, "bf16", "fraction", skew_frac=0.1),
+]
+
+
+@pytest.mark.parametrize("output", [False, True])
+@pytest.mark.parametrize("cache_kind", ["input", "e4m3"])
+@pytest.mark.parametrize("wl", WINDOW, ids=lambda w: w.name)
+def test_window_rows_copied_by_the_row_sweep(wl, cache_kind, output):
+    """The newest min(P, r) rows are copied into their slots by the row
+    statistics (two blocks per unit) or the prompt-output sweep (all blocks),
+    the heavy rows by the selection: every slot row, E4M3 code and scale must
+    match after the prefill, with shares that are empty, ragged or several
+    batches long."""
+    run_workload(wl, wl.units, wl.steps, kv_every=1, prompt_output=output, cache=cache_kind)
+
+
 # ---- ablation policies: static Top-K, naive per-step Top-K, heavy-only (r = 0) ----------
 
 def heavy_only(wl, cid):
