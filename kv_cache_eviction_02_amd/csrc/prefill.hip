@@ -715,7 +715,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
       for (int i = 0; i < 4; ++i) diag[q][sub][i] = sub * kTile + i <= t ? 0.f : -INFINITY;
   }
-  auto soft = [&](auto mask_tag, int ch, f32x4 (&s)[2][QS]) __attribute__((always_inline)) {
+  auto soft = [&](auto mask_tag, auto first_tag, int ch, f32x4 (&s)[2][QS]) __attribute__((always_inline)) {
     if constexpr (decltype(mask_tag)::value) {
 #pragma unroll
       for (int q = 0; q < QS; ++q)
@@ -723,6 +723,26 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int i = 0; i < 4; ++i) s[sub][q][i] += diag[q][sub][i];
+    }
+    if constexpr (decltype(first_tag)::value) {
+      // The wavefront's first chunk (chunk 0): m[q] is still kLow, so every
+      // lane with a kept term would take the retake below.  Its maximum is
+      // taken first instead (kLow for a lane whose terms are all masked),
+      // which is the maximum the retake would set: the same bits, one pass of
+      // exponentials, no rescale (every term is at most 1).
+#pragma unroll
+      for (int q = 0; q < QS; ++q) {
+        float mx = fmaxf(s[0][q][0], s[0][q][1]);
+        mx = fmaxf(fmaxf(mx, s[0][q][2]), s[0][q][3]);
+        mx = fmaxf(fmaxf(mx, s[1][q][0]), s[1][q][1]);
+        mx = fmaxf(fmaxf(mx, s[1][q][2]), s[1][q][3]);
+        m[q] = fmaxf(m[q], mx * sc);
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = fast_exp2(fmaf(s[i >> 2][q][i & 3], sc, -m[q]));
+        l[q] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      }
+      return;
     }
     // Exponentials against the running maximum m[q] without first taking the
     // chunk's maximum.  A lane whose chunk sum exceeds 2^64 (or is infinite,
@@ -762,7 +782,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   // exponentials of chunk ch (S tiles from the stage before) cover their
   // latency, and the MFMAs of chunk ch + 1 then overwrite the same S registers;
   // their results are not needed before the next stage.
-  auto stage = [&](int ch, f32x4 (&s)[2][QS]) __attribute__((always_inline)) {
+  auto stage = [&](auto first_tag, int ch, f32x4 (&s)[2][QS]) __attribute__((always_inline)) {
     const bool diag = ch * RT::KC + RT::KC - 1 > qw0;
     const bool next = active(ch + 1);
     if (ch + 2 < nch) fetch(ch + 2, rk);
@@ -770,9 +790,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     if (next) read(ch + 1, fk);
     if (active(ch)) {
       if (diag)
-        soft(std::true_type{}, ch, s);
+        soft(std::true_type{}, first_tag, ch, s);
       else
-        soft(std::false_type{}, ch, s);
+        soft(std::false_type{}, first_tag, ch, s);
     }
     if (next) mult(fk, s);
     if (ch + 2 < nch) stash(ch & 1, rk);  // chunk ch + 2 replaces chunk ch, read one stage ago
@@ -798,7 +818,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     mult(fk, s);
   }
   __syncthreads();  // every wavefront has read chunk 0 before chunk 2 replaces it
-  for (int ch = 0; ch < nch; ++ch) stage(ch, s);
+  stage(std::true_type{}, 0, s);  // chunk 0 is the first chunk of every wavefront with queries
+  for (int ch = 1; ch < nch; ++ch) stage(std::false_type{}, ch, s);
   win.all(a, unit);
 
   if (qw0 >= P) return;
