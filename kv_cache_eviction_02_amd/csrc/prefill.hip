@@ -745,9 +745,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       return;
     }
     // Exponentials against the running maximum m[q] without first taking the
-    // chunk's maximum.  A lane whose chunk sum exceeds 2^64 (or is infinite,
-    // as on its first chunk, where m[q] is kLow) raises m[q] to the chunk's
-    // maximum and takes the chunk again: rare, and a uniform branch.  Every
+    // chunk's maximum.  A lane whose chunk sum exceeds 2^64 (or is infinite:
+    // a lane whose first chunk was all masked still has m[q] = kLow) raises
+    // m[q] to the chunk's maximum and takes the chunk again: rare, and a
+    // uniform branch.  Every
     // term then stays below 2^64 and one term of the sum is at least 1 (the one
     // that set m[q]), so the float sum keeps its relative precision, and no
     // sum over a row overflows.
