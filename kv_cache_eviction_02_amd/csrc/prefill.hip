@@ -215,35 +215,30 @@ struct RowCopy {
 // p % r), is kept whatever the scores are (H2O summary, "The mechanism": the
 // recent window beside the heavy hitters).  The sweep over query rows (row
 // statistics, or the prompt output) therefore copies its rows into their slots
-// while it runs, a phase that leaves the memory system mostly idle, and the
-// selection afterwards copies only the heavy rows.  The window's rows are split
-// evenly over `ncopy` of a unit's blocks (blk < ncopy).
+// while the launch runs, a phase that leaves the memory system mostly idle,
+// and the selection afterwards copies only the heavy rows.
 //
 // A block that copies pays about one memory latency for it: stores issued
 // mid-sweep make the next tile-load wait also wait for their acknowledgement
 // (vector-memory completions are counted in issue order), and a copy after the
-// sweep waits for its own loads.  The row statistics therefore give the
-// window to the two shortest blocks of each unit (blk 0 and 1), which copy it
-// after their sweep with 8 items (E4M3: 4, at d = 64 2) per thread in flight: measured at
-// opt30b, the sweep then costs what it did without the copy, where copying in
-// all eight blocks cost it 5%.  The prompt-output sweep, whose stages are
-// about twice as long, absorbs a copy split over all its blocks: each thread
-// loads its first batch before the prologue and stores it after the
-// prologue's first barrier (E4M3: after the sweep).  E4M3 rows are quantized
-// one aligned lane group per row.
+// sweep waits for its own loads.  So the window goes to the two shortest blocks
+// of each unit (blk 0 and 1), which copy it after their sweep with 8 items
+// (E4M3: 4, at d = 64 2) per thread in flight.  Measured at opt30b, the row
+// statistics then cost what they did without the copy, where copying in all
+// eight blocks cost them 5%.  E4M3 rows are quantized one aligned lane group
+// per row.
 template <typename T, typename C, int D>
 struct WindowCopy {
   using RC = RowCopy<T, C, D>;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kBatch = 2;  // items per thread in the first batch
-  int first, r, i0, i1;             // window rows start at position `first`; items [i0, i1), item = row * GW + c
-  uint4 kx[kBatch], vx[kBatch];
+  static constexpr int kBlocks = 2;  // blocks of a unit that copy (blk < kBlocks)
+  int first, r, i0, i1;              // window rows start at position `first`; items [i0, i1), item = row * GW + c
 
-  __device__ inline WindowCopy(const PrefillArgs& a, int blk, int nblk, int ncopy) {
+  __device__ inline WindowCopy(const PrefillArgs& a, int blk, int nblk) {
     const int n_ring = min(a.P, a.r);
     first = a.P - n_ring;
     r = a.r;
-    const int nb = min(ncopy, nblk);
+    const int nb = min(kBlocks, nblk);
     i0 = blk < nb ? (int)((long long)n_ring * blk / nb) * RC::GW : 0;
     i1 = blk < nb ? (int)((long long)n_ring * (blk + 1) / nb) * RC::GW : 0;
   }
@@ -254,42 +249,12 @@ struct WindowCopy {
   __device__ inline size_t dst_off(int unit, int k, int i) const {
     return ((size_t)unit * k + pos_of(i) % r) * RC::CROWB + (i % RC::GW) * 16;
   }
-  // Unquantized: loads of the first batch (addresses clamped into the share).
-  __device__ inline void load_first(const PrefillArgs& a, int unit) {
-    if constexpr (!RC::kQuant) {
-      if (i1 > i0) {  // uniform
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const size_t off = src_off(unit, a.P, min(i0 + (int)threadIdx.x + u * kThreads, i1 - 1));
-          kx[u] = load16((const char*)a.pk + off);
-          vx[u] = load16((const char*)a.pv + off);
-        }
-      }
-    }
-  }
-  // Unquantized: stores of the first batch.
-  __device__ inline void store_first(const PrefillArgs& a, int unit) {
-    if constexpr (!RC::kQuant) {
-      if (i1 <= i0) return;  // uniform
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int i = i0 + (int)threadIdx.x + u * kThreads;
-        if (i < i1) {
-          const size_t off = dst_off(unit, a.k, i);
-          store16((char*)a.k_slots + off, kx[u]);
-          store16((char*)a.v_slots + off, vx[u]);
-        }
-      }
-    }
-  }
-  // Unquantized items [from, i1) of the share, RB per thread in flight; or the
-  // whole share quantized to E4M3 codes and per-row scales.  Called by every
-  // thread of the block.
-  template <int RB>
-  __device__ inline void copy(const PrefillArgs& a, int unit, int from) {
+  // This block's share, after its sweep.  Called by every thread of the block.
+  __device__ inline void copy(const PrefillArgs& a, int unit) {
     const int tid = threadIdx.x;
     if constexpr (!RC::kQuant) {
-      for (int base = from; base < i1; base += RB * kThreads) {
+      constexpr int RB = 8;  // items per thread loaded before any is stored
+      for (int base = i0; base < i1; base += RB * kThreads) {
         uint4 kb[RB], vb[RB];
 #pragma unroll
         for (int u = 0; u < RB; ++u) {
@@ -309,9 +274,9 @@ struct WindowCopy {
       }
     } else {
       // i0 and i1 are whole rows and GW divides the block, so a row's lane
-      // group is in or out together.  The loads of RB items per thread are
+      // group is in or out together.  The loads of QB items per thread are
       // issued before any of them is quantized.
-      constexpr int QB = RB < 4 ? RB : (D >= 96 ? 4 : 2);  // d = 64: 2 keeps the sweep's occupancy
+      constexpr int QB = D >= 96 ? 4 : 2;  // d = 64: 2 keeps the row statistics' occupancy
       for (int base = i0; base < i1; base += QB * kThreads) {
         uint4 x[QB][4];
 #pragma unroll
@@ -327,10 +292,6 @@ struct WindowCopy {
       }
     }
   }
-  // After load_first / store_first: the rest of the share.
-  __device__ inline void rest(const PrefillArgs& a, int unit) { copy<kBatch>(a, unit, i0 + kBatch * kThreads); }
-  // The whole share, after the sweep.
-  __device__ inline void all(const PrefillArgs& a, int unit) { copy<8>(a, unit, i0); }
 };
 
 // ---- prompt attention output --------------------------------------------------
@@ -414,8 +375,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const char* Vb = (const char*)a.pv + (size_t)unit * P * AT::ROWB;
   const float sc = a.scale_log2;
 
-  WindowCopy<T, C, D> win(a, blk, nblk, nblk);
-  win.load_first(a, unit);
   Frag<T, D> fq[QS];
 #pragma unroll
   for (int q = 0; q < QS; ++q) fq[q].load(Qb, qw0 + q * kTile, P, lane);
@@ -557,7 +516,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   fetch(0);
   stash(0, 0);
   __syncthreads();
-  win.store_first(a, unit);
   for (int ch = 0; ch < nch; ++ch) {
     if (ch + 1 < nch) fetch(ch + 1);
     const char* kl = smem + (ch % AT::NBUF) * AT::BUF;
@@ -566,7 +524,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     if (ch + 1 < nch) stash(ch + 1, (ch + 1) % AT::NBUF);
     __syncthreads();
   }
-  win.rest(a, unit);
+  WindowCopy<T, C, D>(a, blk, nblk).copy(a, unit);
 
   if (qw0 >= P) return;
 #pragma unroll
@@ -646,7 +604,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const char* Kb = (const char*)a.pk + (size_t)unit * P * RT::ROWB;
   const float sc = pin_arg(a.scale_log2);
 
-  WindowCopy<T, C, D> win(a, blk, nblk, 2);
   Frag<T, D> fq[QS];
 #pragma unroll
   for (int q = 0; q < QS; ++q) fq[q].load_clamped(Qb, qw0 + q * kTile, P, lane);  // rows past P: not written
@@ -821,7 +778,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   __syncthreads();  // every wavefront has read chunk 0 before chunk 2 replaces it
   stage(std::true_type{}, 0, s);  // chunk 0 is the first chunk of every wavefront with queries
   for (int ch = 1; ch < nch; ++ch) stage(std::false_type{}, ch, s);
-  win.all(a, unit);
+  WindowCopy<T, C, D>(a, blk, nblk).copy(a, unit);
 
   if (qw0 >= P) return;
 #pragma unroll
