@@ -26,7 +26,8 @@
 // shared by a block's four wavefronts, staged through registers one stage
 // ahead.  In each stage a wavefront reads the next chunk's fragments from LDS,
 // runs the current chunk's exponentials while they arrive, then the next
-// chunk's MFMAs.
+// chunk's MFMAs.  A unit's blocks run on one XCD, longest first; the last
+// units of each XCD's range are interleaved so that no long block starts last.
 //
 // MFMA use: v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (f32).
 // Lane l supplies row l % 16 of a 16-row tile; of each 64-byte piece i of the
